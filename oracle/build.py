@@ -1,0 +1,31 @@
+"""Build the fp64 CPU oracle (plain C, gcc + OpenMP) into a shared library.
+
+Test infrastructure only: the product library never loads what this builds.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "kda_oracle.c")
+LIBRARY = os.path.join(HERE, "libkda_oracle.so")
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, quiet: bool = True) -> str:
+    """Compile `source` with gcc into `output`; returns the library path."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Werror", source, "-o", output + ".tmp", "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(output + ".tmp", output)
+    if not quiet:
+        print("built", output)
+    return output
+
+
+if __name__ == "__main__":
+    build(quiet=False)
+    sys.exit(0)

@@ -1,0 +1,19 @@
+"""Shared pytest configuration.
+
+Tests marked `gpu` need an MI355X and the built HIP library; everything else
+runs on the CPU (the oracle, its pins, host-side validation and the library's
+symbol table).
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD GPU (gfx950) and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test")

@@ -1,0 +1,81 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+every broken copy to fail at least one pin.  This shows the pins constrain
+every part of the oracle: the decay, the projection, the write, the output
+read, checkpoints, initial state, the conv filter and state, and the norm."""
+import os
+import re
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from tests.oracle_pins import ALL_PINS
+
+with open(obuild.SOURCE) as _f:
+    SOURCE = _f.read()
+
+
+def _swap_decay_and_projection(src):
+    a = src.index("    /* S <- Diag(alpha) S")
+    b = src.index("    /* S <- (I - beta k k^T) S")
+    c = src.index("    /* S <- S + beta k v^T. */")
+    return src[:a] + src[b:c] + src[a:b] + src[c:]
+
+
+def _output_before_update(src):
+    a = src.index("    /* o = scale * S^T q. */")
+    end = src.index("\n}\n", a)
+    block = src[a:end + 1]
+    body = src[:a] + src[end + 1:]
+    start = body.index("    /* S <- Diag(alpha) S")
+    return body[:start] + block + body[start:]
+
+
+def _sub(old, new, count=1):
+    def f(src):
+        assert src.count(old) >= 1, old
+        return src.replace(old, new, count)
+    return f
+
+
+MUTANTS = {
+    "decay_sign": _sub("double a = exp(g[i]);", "double a = exp(-g[i]);"),
+    "decay_after_projection": _swap_decay_and_projection,
+    "output_before_update": _output_before_update,
+    "projection_without_beta": _sub("S[i * dv + j] -= beta * k[i] * work[j];",
+                                    "S[i * dv + j] -= k[i] * work[j];"),
+    "write_without_beta": _sub("S[i * dv + j] += beta * k[i] * v[j];",
+                               "S[i * dv + j] += k[i] * v[j];"),
+    "projection_uses_q": _sub("s += k[i] * S[i * dv + j];", "s += q[i] * S[i * dv + j];"),
+    "scale_dropped": _sub("o[j] = scale * s;", "o[j] = s;"),
+    "checkpoint_off_by_one": _sub("(r + 1) % ckpt_interval == 0", "r % ckpt_interval == 0"),
+    "initial_state_ignored": _sub("if (!has_init || has_init[i]) memcpy(S, home",
+                                  "if (1) memcpy(S, home"),
+    "state_not_written": _sub("memcpy(home, S,", "if (0) memcpy(home, S,"),
+    "padding_not_zeroed": _sub("memset(o + (t * H + h) * dv, 0,", "if (0) memset(o + (t * H + h) * dv, 0,"),
+    "l2norm_skipped_for_k": _sub("kt = kn;", "kt = kt;"),
+    "conv_taps_reversed": _sub("acc += w[c * W + j] * ext", "acc += w[c * W + (W - 1 - j)] * ext"),
+    "conv_state_not_updated": _sub("memcpy(st, ext + L * Cch,", "if (0) memcpy(st, ext + L * Cch,"),
+    "conv_state_ignored": _sub("if (!has_init || has_init[i]) memcpy(ext, st,",
+                               "if (0) memcpy(ext, st,"),
+    "rmsnorm_sum_not_mean": _sub("ss / (double)dim + eps", "ss + eps"),
+    "rmsnorm_sigmoid_not_silu": _sub("double act = z / (1.0 + exp(-z));",
+                                     "double act = 1.0 / (1.0 + exp(-z));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name, tmp_path):
+    src = MUTANTS[name](SOURCE)
+    assert src != SOURCE
+    path = tmp_path / f"mutant_{name}.c"
+    path.write_text(src)
+    lib = obuild.build(str(path), str(tmp_path / f"libmutant_{name}.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
