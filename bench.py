@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  The headline `value` is chunk-prefill throughput in
+tokens/s on the single-sequence workload (T=4096, H=16, d_k=d_v=128, C=64,
+bf16 q/k/v, fp32 g/beta, fp32 state in slot 7 of a 64-slot pool), timed over
+exactly K back-to-back calls after W warm-up calls, with torch.cuda.synchronize
+on both sides.  To keep the inputs coming from HBM rather than from the 256 MB
+last-level cache, the calls rotate over four independent copies of the
+activations (each ~80 MB).  The same line carries:
+  * decode: seq/s for 512 sequences x 1 token on an fp32 pool of 1024 slots;
+  * pipeline: tokens/s of one 4096-token call of the long-context pipeline
+    (conv1d -> prefill with q/k L2 norm, bf16 state, checkpoint -> gated RMSNorm);
+  * roofline objects (algorithmic bytes / measured time against 8 TB/s);
+  * cpu_baseline: the fp64 oracle timed on the host on the same prefill
+    workload (bounded to ~10 s).
+Only one GPU is supported: --gpus other than 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def prefill_alg_bytes(T: int, H: int, dk: int, dv: int, act_bytes: int, state_bytes: int,
+                      n_states: int) -> int:
+    """q, k, v, o in the activation dtype, g fp32 per key channel, beta fp32,
+    plus each touched state read and written once."""
+    per_token_head = (2 * dk + 2 * dv) * act_bytes + 4 * dk + 4
+    return T * H * per_token_head + 2 * n_states * H * dk * dv * state_bytes
+
+
+def prefill_alg_flops(T: int, H: int, d: int, C: int) -> float:
+    """Chunked method, triangles counted once: 6Cd^2 + C^2(3d + 2d) + C^3/3 per chunk."""
+    per_chunk = 6 * C * d * d + C * C * (3 * d + 2 * d) + C ** 3 / 3
+    return per_chunk / C * T * H
+
+
+def decode_alg_bytes(B: int, H: int, dk: int, dv: int, act_bytes: int, state_bytes: int) -> int:
+    per_seq_head = 2 * dk * dv * state_bytes + (2 * dk + 2 * dv) * act_bytes + 4 * dk + 4
+    return B * H * per_seq_head
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` calls with HIP events on the current
+    stream (the stream the kernels run on), bracketed by synchronize."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+    from gated_delta_rule_42_amd import kda, workloads as wl
+    case = wl.single_seq_prefill()
+    dev = "cuda"
+    n_sets = 4
+    sets = []
+    for s in range(n_sets):
+        # Independent copies (identical values) so that consecutive calls do
+        # not find their inputs in the last-level cache.
+        sets.append([t.to(dev).clone() for t in (case.q, case.k, case.v, case.g, case.beta)])
+    cu, slots = case.cu_seqlens.to(dev), case.slots.to(dev)
+    pool = case.pool.to(dev)
+    T, H, d = 4096, 16, 128
+    out = torch.empty(T, H, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(1, T, H, d, d, 64), dtype=torch.uint8,
+                     device=dev)
+
+    def call(i):
+        q, k, v, g, beta = sets[i % n_sets]
+        kda.chunk_prefill(q, k, v, g, beta, cu, pool, slots, out, workspace=ws, chunk_size=64)
+
+    ms, wall = time_calls(call, steps, warmup)
+    return case, ms, wall
+
+
+def bench_decode(steps: int, warmup: int):
+    import torch
+    from gated_delta_rule_42_amd import kda, workloads as wl
+    case = wl.decode_batch()
+    dev = "cuda"
+    q, k, v, g, beta = (t.to(dev) for t in (case.q, case.k, case.v, case.g, case.beta))
+    pool = case.pool.to(dev)
+    slots = case.slots.to(dev)
+    out = torch.empty_like(v)
+
+    def call(i):
+        kda.recurrent_decode(q, k, v, g, beta, pool, slots, out)
+
+    ms, wall = time_calls(call, steps, warmup)
+    return case, ms, wall
+
+
+def bench_pipeline(steps: int, warmup: int):
+    import torch
+    from gated_delta_rule_42_amd import kda, workloads as wl
+    lc = wl.long_context()
+    dev = "cuda"
+    T, H, d = lc.T_call, lc.H, lc.d
+    c0 = lc.call(0)
+    x, g, beta, gate = (t.to(dev) for t in (c0.x, c0.g, c0.beta, c0.gate))
+    w = lc.conv_weight.to(dev)
+    nw = lc.norm_weight.to(dev)
+    conv_pool = torch.zeros(lc.n_slots, lc.conv_width - 1, lc.channels, dtype=torch.bfloat16,
+                            device=dev)
+    pool = torch.zeros(lc.n_slots, H, d, d, dtype=torch.bfloat16, device=dev)
+    ckpt = torch.empty(1, H, d, d, dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    slot = torch.tensor([lc.state_slot], dtype=torch.int32, device=dev)
+    y = torch.empty(T, lc.channels, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(T, H, d, dtype=torch.bfloat16, device=dev)
+    z = torch.empty_like(o)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(1, T, H, d, d, 64), dtype=torch.uint8,
+                     device=dev)
+    hd = H * d
+
+    def call(i):
+        kda.causal_conv1d(x, w, cu, conv_pool, slot, y)
+        kda.chunk_prefill(y[:, :hd].view(T, H, d), y[:, hd:2 * hd].view(T, H, d),
+                          y[:, 2 * hd:].view(T, H, d), g, beta, cu, pool, slot, o, workspace=ws,
+                          checkpoints=ckpt, ckpt_interval=T, chunk_size=64,
+                          flags=kda.KDA_FLAG_QK_L2NORM)
+        kda.gated_rmsnorm(o, gate, z, weight=nw, eps=lc.eps)
+
+    ms, wall = time_calls(call, steps, warmup)
+    return lc, ms, wall
+
+
+def cpu_baseline(case, budget_s: float = 10.0):
+    """The fp64 oracle (as it stands) on the same prefill workload, repeated
+    until `budget_s` has passed (at least once)."""
+    import oracle
+    f = lambda t: t.double().numpy()
+    args = [f(t) for t in (case.q, case.k, case.v, case.g, case.beta)]
+    pool = f(case.pool)
+    cu, slots = case.cu_seqlens.numpy(), case.slots.numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(*args, cu, pool, slots)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    units = case.num_seqs * case.q.shape[1]
+    return {"value": case.total_tokens * reps / el, "unit": "tokens/s",
+            "cores": min(oracle.num_threads(), units), "kind": "oracle",
+            "sample": f"full prefill workload (T={case.total_tokens}, H={case.q.shape[1]}, "
+                      f"d=128) x{reps} calls in {el:.1f} s; OpenMP over the {units} "
+                      f"(sequence, head) units"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["prefill", "decode", "pipeline"], default=None,
+                    help="run one leg only (for profiling); prints that leg's numbers")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    K, W = args.steps, args.warmup
+    result = {}
+    if args.only in (None, "prefill"):
+        case, ms, wall = bench_prefill(K, W)
+        T, H, d = 4096, 16, 128
+        nbytes = prefill_alg_bytes(T, H, d, d, 2, 4, 1)
+        flops = prefill_alg_flops(T, H, d, 64)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        result.update({
+            "metric": "KDA prefill tokens/s (T=4096,H=16,d=128) + decode seq/s; % MFMA/HBM roofline",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+            "ms_per_step": ms, "wall_s_timed": wall, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": case.name, "seqs": 1, "seq_len": T, "heads": H, "d_k": d,
+                       "d_v": d, "chunk": 64, "act": "bf16", "g_beta": "fp32",
+                       "state": "fp32 pool[64] slot 7", "parallelism": "none (1 GPU)"},
+            "roofline": {"kernel": "kda_chunk_prefill (intra_kernel + chain_kernel)",
+                         "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "alg_bytes": nbytes, "alg_flops": flops,
+                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        })
+    if args.only in (None, "decode"):
+        dcase, dms, dwall = bench_decode(K, W)
+        B, H, d = 512, 16, 128
+        dbytes = decode_alg_bytes(B, H, d, d, 2, 4)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "value": B / (dms * 1e-3), "unit": "seq/s", "ms_per_step": dms, "steps": K,
+            "workload": dcase.name,
+            "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": dgbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                         "traffic": None, "alg_bytes": dbytes}}
+    if args.only in (None, "pipeline"):
+        lc, pms, pwall = bench_pipeline(K, W)
+        result["pipeline"] = {
+            "value": lc.T_call / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms,
+            "steps": K, "workload": lc.name + " (one 4096-token call per step)"}
+    if args.only in (None, "prefill") and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case)
+    if args.only is not None and "value" not in result:
+        leg = result[args.only]
+        result = {"metric": args.only, **leg}
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

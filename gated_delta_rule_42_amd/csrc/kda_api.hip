@@ -1,0 +1,203 @@
+// kda_api.hip -- the C ABI declared in include/kda.h: argument validation and
+// dispatch to the kernel launchers.  Every check here runs on the host before
+// any HIP call, so a rejected call enqueues nothing and touches no device.
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
+bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64; }
+
+kda_status_t launch_status(hipError_t e)
+{
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status_t status)
+{
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype, chunk size or interval";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                        int32_t num_heads, int32_t dk, int32_t dv,
+                                        int32_t chunk_size)
+{
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return 0;
+    if (!dim_ok(dk) || dk != dv || !chunk_ok(chunk_size)) return 0;
+    return kda::prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv, chunk_size);
+}
+
+kda_status_t kda_chunk_prefill(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || num_slots < 0 ||
+        ckpt_capacity < 0 || ckpt_interval < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(act_dtype) || !dtype_ok(state_dtype)) return KDA_ERR_INVALID_ARG;
+    if (flags & ~KDA_FLAG_QK_L2NORM) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || dk != dv || !chunk_ok(chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_interval > 0 && ckpt_interval % chunk_size != 0) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return KDA_OK;
+    if (!cu_seqlens || !state_indices) return KDA_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
+    if (num_slots > 0 && !state_pool) return KDA_ERR_INVALID_ARG;
+    if (ckpt_interval > 0 && ckpt_capacity > 0 && !checkpoints) return KDA_ERR_INVALID_ARG;
+    const int64_t hk = (int64_t)num_heads * dk, hv = (int64_t)num_heads * dv;
+    if (q_stride_t < hk || k_stride_t < hk || v_stride_t < hv || out_stride_t < hv)
+        return KDA_ERR_INVALID_ARG;
+    if ((q_stride_t | k_stride_t | v_stride_t | out_stride_t) & 7) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(out) ||
+        !aligned16(state_pool) || !aligned16(checkpoints))
+        return KDA_ERR_INVALID_ARG;
+    const size_t need = kda::prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv,
+                                                     chunk_size);
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return KDA_ERR_INVALID_ARG;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.q_stride = q_stride_t; a.k_stride = k_stride_t; a.v_stride = v_stride_t;
+    a.g = g; a.beta = beta;
+    a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+    a.heads = num_heads; a.dk = dk; a.dv = dv;
+    a.pool = state_pool; a.num_slots = num_slots;
+    a.slots = state_indices; a.has_init = has_initial_state;
+    a.ckpt = (ckpt_interval > 0) ? checkpoints : nullptr;
+    a.ckpt_capacity = (ckpt_interval > 0 && checkpoints) ? ckpt_capacity : 0;
+    a.ckpt_interval = ckpt_interval;
+    a.scale = scale; a.chunk = chunk_size; a.flags = flags;
+    a.out = out; a.out_stride = out_stride_t;
+    a.workspace = workspace;
+    a.act = act_dtype; a.state = state_dtype;
+    return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_recurrent_decode(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_b, int64_t k_stride_b, int64_t v_stride_b,
+    const float* g, const float* beta,
+    int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, float scale, uint32_t flags,
+    void* out, int64_t out_stride_b, void* stream)
+{
+    if (batch < 0 || num_heads <= 0 || num_slots < 0) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(act_dtype) || !dtype_ok(state_dtype)) return KDA_ERR_INVALID_ARG;
+    if (flags & ~KDA_FLAG_QK_L2NORM) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || dk != dv) return KDA_ERR_UNSUPPORTED;
+    if (batch == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state_indices || !out) return KDA_ERR_INVALID_ARG;
+    if (num_slots > 0 && !state_pool) return KDA_ERR_INVALID_ARG;
+    const int64_t hk = (int64_t)num_heads * dk, hv = (int64_t)num_heads * dv;
+    if (q_stride_b < hk || k_stride_b < hk || v_stride_b < hv || out_stride_b < hv)
+        return KDA_ERR_INVALID_ARG;
+    if ((q_stride_b | k_stride_b | v_stride_b | out_stride_b) & 7) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(state_pool))
+        return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.q_stride = q_stride_b; a.k_stride = k_stride_b; a.v_stride = v_stride_b;
+    a.g = g; a.beta = beta;
+    a.batch = batch; a.heads = num_heads; a.dk = dk; a.dv = dv;
+    a.pool = state_pool; a.num_slots = num_slots; a.slots = state_indices;
+    a.scale = scale; a.flags = flags;
+    a.out = out; a.out_stride = out_stride_b;
+    a.act = act_dtype; a.state = state_dtype;
+    return launch_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_gated_rmsnorm(
+    const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
+    const void* weight, void* y, int64_t y_stride_t, kda_dtype_t dtype,
+    int64_t tokens, int32_t heads, int32_t dim, float eps, void* stream)
+{
+    if (tokens < 0 || heads <= 0 || !(eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (dim <= 0 || dim > 1024 || dim % 8 != 0) return KDA_ERR_UNSUPPORTED;
+    if (tokens == 0) return KDA_OK;
+    if (!x || !gate || !y) return KDA_ERR_INVALID_ARG;
+    const int64_t hd = (int64_t)heads * dim;
+    if (x_stride_t < hd || gate_stride_t < hd || y_stride_t < hd) return KDA_ERR_INVALID_ARG;
+    if ((x_stride_t | gate_stride_t | y_stride_t) & 7) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(gate) || !aligned16(y) || !aligned16(weight))
+        return KDA_ERR_INVALID_ARG;
+
+    kda::RmsNormArgs a;
+    a.x = x; a.x_stride = x_stride_t;
+    a.gate = gate; a.gate_stride = gate_stride_t;
+    a.weight = weight;
+    a.y = y; a.y_stride = y_stride_t;
+    a.tokens = tokens; a.heads = heads; a.dim = dim;
+    a.eps = eps; a.dtype = dtype;
+    return launch_status(kda::launch_gated_rmsnorm(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_causal_conv1d(
+    const void* x, int64_t x_stride_t, const void* weight, const void* bias,
+    void* conv_state_pool, int64_t num_slots,
+    const int32_t* cu_seqlens, const int32_t* state_indices,
+    const uint8_t* has_initial_state, int32_t num_seqs, int64_t total_tokens,
+    int32_t channels, int32_t width, kda_dtype_t dtype, uint32_t flags,
+    void* y, int64_t y_stride_t, void* stream)
+{
+    if (num_seqs < 0 || total_tokens < 0 || num_slots < 0 || channels <= 0)
+        return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (flags & ~KDA_CONV_SILU) return KDA_ERR_INVALID_ARG;
+    if (width < 2 || width > 8 || channels % 8 != 0) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return KDA_OK;
+    if (!cu_seqlens || !state_indices || !weight) return KDA_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!x || !y)) return KDA_ERR_INVALID_ARG;
+    if (num_slots > 0 && !conv_state_pool) return KDA_ERR_INVALID_ARG;
+    if (x_stride_t < channels || y_stride_t < channels) return KDA_ERR_INVALID_ARG;
+    if ((x_stride_t | y_stride_t) & 7) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(conv_state_pool) || !aligned16(weight) ||
+        !aligned16(bias))
+        return KDA_ERR_INVALID_ARG;
+
+    kda::ConvArgs a;
+    a.x = x; a.x_stride = x_stride_t;
+    a.weight = weight; a.bias = bias;
+    a.state = conv_state_pool; a.num_slots = num_slots;
+    a.cu_seqlens = cu_seqlens; a.slots = state_indices; a.has_init = has_initial_state;
+    a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+    a.channels = channels; a.width = width; a.flags = flags;
+    a.y = y; a.y_stride = y_stride_t;
+    a.dtype = dtype;
+    return launch_status(kda::launch_causal_conv1d(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// kda_device.cuh -- device helpers shared by the KDA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Scalar conversions.  bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest
+// even (the language's conversion; gfx950 has a native instruction for it).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// ---------------------------------------------------------------------------
+// Vector I/O of 4 consecutive elements (16 B for fp32, 8 B for bf16).  The
+// address must be aligned to the vector size.
+__device__ __forceinline__ void load4(const float* p, float (&x)[4])
+{
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float (&x)[4])
+{
+    const bf16x4 t = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = static_cast<float>(t[i]);
+}
+__device__ __forceinline__ void store4(float* p, const float (&x)[4])
+{
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store4(bf16* p, const float (&x)[4])
+{
+    bf16x4 t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = static_cast<bf16>(x[i]);
+    *reinterpret_cast<bf16x4*>(p) = t;
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (64 lanes).
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers.
+//
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
+//   A: lane l supplies row (l % 16), 8 K-elements of lane group (l / 16).
+//   B: lane l supplies column (l % 16), the same 8 K-elements.
+//   C/D: lane l holds column (l % 16), rows 4*(l/16) .. 4*(l/16)+3.
+// A and B name their K-elements the same way, so any consistent relabelling
+// of K (used to feed accumulators straight back in as B operands) leaves the
+// product unchanged.
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x4_f32: D[16x16] += A[16x4] * B[4x16] in fp32.
+//   A: lane l supplies A[l % 16][l / 16]; B: lane l supplies B[l / 16][l % 16].
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8])
+{
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<bf16>(x[i]);
+    return r;
+}
+
+}  // namespace kda

@@ -1,0 +1,69 @@
+// kda_internal.h -- launcher interfaces between the C-ABI layer (kda_api.hip)
+// and the kernel translation units.  Host code only; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+struct DecodeArgs {
+    const void* q; const void* k; const void* v;
+    int64_t q_stride, k_stride, v_stride;       // elements between rows
+    const float* g; const float* beta;
+    int32_t batch, heads, dk, dv;
+    void* pool; int64_t num_slots;
+    const int32_t* slots;
+    float scale; uint32_t flags;
+    void* out; int64_t out_stride;
+    kda_dtype_t act, state;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+    const void* q; const void* k; const void* v;
+    int64_t q_stride, k_stride, v_stride;        // elements between tokens
+    const float* g; const float* beta;
+    const int32_t* cu_seqlens; int32_t num_seqs; int64_t total_tokens;
+    int32_t heads, dk, dv;
+    void* pool; int64_t num_slots;
+    const int32_t* slots; const uint8_t* has_init;
+    void* ckpt; int64_t ckpt_capacity; int32_t ckpt_interval;
+    float scale; int32_t chunk; uint32_t flags;
+    void* out; int64_t out_stride;
+    void* workspace;
+    kda_dtype_t act, state;
+};
+// Workspace bytes for a call; 0 if the shape is unsupported.
+size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t heads,
+                               int32_t dk, int32_t dv, int32_t chunk);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct RmsNormArgs {
+    const void* x; int64_t x_stride;
+    const void* gate; int64_t gate_stride;
+    const void* weight;
+    void* y; int64_t y_stride;
+    int64_t tokens; int32_t heads, dim;
+    float eps;
+    kda_dtype_t dtype;
+};
+hipError_t launch_gated_rmsnorm(const RmsNormArgs& a, hipStream_t stream);
+
+struct ConvArgs {
+    const void* x; int64_t x_stride;
+    const void* weight; const void* bias;
+    void* state; int64_t num_slots;
+    const int32_t* cu_seqlens; const int32_t* slots; const uint8_t* has_init;
+    int32_t num_seqs; int64_t total_tokens;
+    int32_t channels, width;
+    uint32_t flags;
+    void* y; int64_t y_stride;
+    kda_dtype_t dtype;
+};
+hipError_t launch_causal_conv1d(const ConvArgs& a, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,218 @@
+"""Thin ctypes binding of libkda.so (include/kda.h): the same entry points,
+taking torch tensors.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkda.so.  PyTorch supplies device memory and the stream.  If the
+library is missing, importing this module raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE_TOO_SMALL = 3
+KDA_ERR_LAUNCH = 4
+
+KDA_F32 = 0
+KDA_BF16 = 1
+KDA_FLAG_QK_L2NORM = 1
+KDA_CONV_SILU = 1
+
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {message} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing; build it with "
+                          "`python -m gated_delta_rule_42_amd.build`")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i32, i64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t)
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_abi_version.argtypes = []
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_chunk_prefill_workspace_size.restype = sz
+    lib.kda_chunk_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.kda_chunk_prefill.restype = i32
+    lib.kda_chunk_prefill.argtypes = [
+        vp, vp, vp, i32, i64, i64, i64, vp, vp,
+        vp, i32, i64, i32, i32, i32,
+        vp, i32, i64, vp, vp,
+        vp, i64, i32,
+        f32, i32, u32, vp, i64, vp, sz, vp]
+    lib.kda_recurrent_decode.restype = i32
+    lib.kda_recurrent_decode.argtypes = [
+        vp, vp, vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, i32,
+        vp, i32, i64, vp, f32, u32, vp, i64, vp]
+    lib.kda_gated_rmsnorm.restype = i32
+    lib.kda_gated_rmsnorm.argtypes = [vp, i64, vp, i64, vp, vp, i64, i32, i64, i32, i32, f32, vp]
+    lib.kda_causal_conv1d.restype = i32
+    lib.kda_causal_conv1d.argtypes = [
+        vp, i64, vp, vp, vp, i64, vp, vp, vp, i32, i64, i32, i32, i32, u32, vp, i64, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != KDA_OK:
+        raise KdaError(fn, status, _lib.kda_status_string(status).decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _token_stride(t: torch.Tensor, name: str) -> int:
+    """[tokens, heads, dim] with heads packed inside a token: stride (s, dim, 1)."""
+    if t.dim() == 3 and t.numel() == 0:
+        return t.shape[1] * t.shape[2]
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [tokens, heads, dim] with contiguous heads")
+    return t.stride(0)
+
+
+def _contig(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous {dtype}")
+
+
+def abi_version() -> int:
+    return int(_lib.kda_abi_version())
+
+
+def status_string(status: int) -> str:
+    return _lib.kda_status_string(status).decode()
+
+
+def chunk_prefill_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int,
+                                 dv: int, chunk_size: int = 64) -> int:
+    return int(_lib.kda_chunk_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv,
+                                                     chunk_size))
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, *,
+                  workspace=None, has_initial_state=None, checkpoints=None,
+                  ckpt_interval: int = 0, scale: float = 1.0, chunk_size: int = 64,
+                  flags: int = 0, stream=None) -> None:
+    """kda_chunk_prefill.  q,k [T,H,dk]; v,out [T,H,dv] (token-strided views
+    allowed); g [T,H,dk] fp32; beta [T,H] fp32; cu_seqlens [N+1] int32;
+    state_pool [slots,H,dk,dv] fp32/bf16 (updated in place); state_indices [N]
+    int32; has_initial_state [N] uint8 or None; checkpoints [cap,H,dk,dv] or
+    None.  `workspace` is a uint8 tensor of at least
+    chunk_prefill_workspace_size(...) bytes; None allocates one."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = state_indices.numel()
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    _contig(cu_seqlens, "cu_seqlens", torch.int32)
+    _contig(state_indices, "state_indices", torch.int32)
+    if has_initial_state is not None:
+        _contig(has_initial_state, "has_initial_state", torch.uint8)
+    if not state_pool.is_contiguous():
+        raise ValueError("state_pool must be contiguous")
+    need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    cap = 0
+    if checkpoints is not None:
+        if not checkpoints.is_contiguous() or checkpoints.dtype != state_pool.dtype:
+            raise ValueError("checkpoints must be contiguous with the state dtype")
+        cap = checkpoints.shape[0]
+    status = _lib.kda_chunk_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q),
+        _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v"),
+        _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+        _ptr(state_pool), _dtype(state_pool), state_pool.shape[0] if state_pool.dim() else 0,
+        _ptr(state_indices), _ptr(has_initial_state),
+        _ptr(checkpoints), cap, int(ckpt_interval),
+        float(scale), int(chunk_size), int(flags),
+        _ptr(out), _token_stride(out, "out"),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("kda_chunk_prefill", status)
+
+
+def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, out, *, scale: float = 1.0,
+                     flags: int = 0, stream=None) -> None:
+    """kda_recurrent_decode.  q,k [B,H,dk]; v,out [B,H,dv] (row-strided views
+    allowed); g [B,H,dk] fp32; beta [B,H] fp32; state_pool updated in place."""
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    _contig(state_indices, "state_indices", torch.int32)
+    if not state_pool.is_contiguous():
+        raise ValueError("state_pool must be contiguous")
+    status = _lib.kda_recurrent_decode(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q),
+        _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v"),
+        _ptr(g), _ptr(beta), B, H, dk, dv,
+        _ptr(state_pool), _dtype(state_pool), state_pool.shape[0],
+        _ptr(state_indices), float(scale), int(flags), _ptr(out), _token_stride(out, "out"),
+        _stream(stream))
+    _check("kda_recurrent_decode", status)
+
+
+def gated_rmsnorm(x, gate, y, *, weight=None, eps: float = 1e-6, stream=None) -> None:
+    """kda_gated_rmsnorm on [T,H,dim] (token-strided views allowed)."""
+    T, H, dim = x.shape
+    if weight is not None:
+        _contig(weight, "weight", x.dtype)
+    status = _lib.kda_gated_rmsnorm(
+        _ptr(x), _token_stride(x, "x"), _ptr(gate), _token_stride(gate, "gate"),
+        _ptr(weight), _ptr(y), _token_stride(y, "y"), _dtype(x), T, H, dim, float(eps),
+        _stream(stream))
+    _check("kda_gated_rmsnorm", status)
+
+
+def causal_conv1d(x, weight, cu_seqlens, conv_state_pool, state_indices, y, *, bias=None,
+                  has_initial_state=None, silu: bool = True, stream=None) -> None:
+    """kda_causal_conv1d.  x,y [T,C] (token stride allowed, channels
+    contiguous); weight [C,W]; conv_state_pool [slots,W-1,C] updated in place."""
+    T, C = x.shape
+    W = weight.shape[1]
+    if x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("x and y need contiguous channels")
+    _contig(weight, "weight", x.dtype)
+    _contig(cu_seqlens, "cu_seqlens", torch.int32)
+    _contig(state_indices, "state_indices", torch.int32)
+    if has_initial_state is not None:
+        _contig(has_initial_state, "has_initial_state", torch.uint8)
+    if not conv_state_pool.is_contiguous() or conv_state_pool.dtype != x.dtype:
+        raise ValueError("conv_state_pool must be contiguous with x's dtype")
+    status = _lib.kda_causal_conv1d(
+        _ptr(x), x.stride(0), _ptr(weight), _ptr(bias), _ptr(conv_state_pool),
+        conv_state_pool.shape[0], _ptr(cu_seqlens), _ptr(state_indices),
+        _ptr(has_initial_state), state_indices.numel(), T, C, W, _dtype(x),
+        KDA_CONV_SILU if silu else 0, _ptr(y), y.stride(0), _stream(stream))
+    _check("kda_causal_conv1d", status)

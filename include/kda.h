@@ -1,0 +1,222 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * Kimi Delta Attention (KDA) is the gated delta rule with a per-key-channel
+ * decay.  For each head the state S is a d_k x d_v matrix and each token does
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * The pages name this operator and split it into a chunk prefill and a
+ * recurrent decode (page "[Feature][KDA] Add Kimi K3 KDA execution", What this
+ * PR does and KDA execution steps 3-4).  Around the two sit the causal
+ * convolution that feeds them (step 2) and the gated RMSNorm applied to their
+ * output (What this PR does).
+ *
+ * Conventions for every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller, except
+ *     where a comment says otherwise.  The library allocates nothing, keeps no
+ *     state between calls and never synchronises: each call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream), so it can
+ *     be captured into a HIP graph.  Outputs are valid once the stream has
+ *     reached that point.
+ *   - Layouts are row-major.  Activations are [tokens, heads, dim] with the
+ *     head blocks of one token contiguous and a caller-given token stride (in
+ *     elements), so packed projections can be read in place.  Recurrent
+ *     states are [slots, heads, d_k, d_v] with d_v contiguous.
+ *   - Inputs are read-only.  Outputs must not alias inputs.
+ *   - Only errors the host can see are reported: a bad argument returns a
+ *     status without enqueuing anything; a failed launch returns
+ *     KDA_ERR_LAUNCH.  Device-side data (cu_seqlens, slot indices) are a
+ *     caller contract: cu_seqlens must be non-decreasing with
+ *     cu_seqlens[0] = 0 and cu_seqlens[num_seqs] <= total_tokens, slot
+ *     indices must be < num_slots and distinct within a call (< 0 marks a
+ *     padding row).  The kernels clamp what they can so that a violation
+ *     corrupts results rather than memory, but results are then undefined.
+ *   - Results are deterministic: the same call on the same inputs gives
+ *     bitwise identical outputs and states (no floating-point atomics), and
+ *     which pool slot a sequence uses does not change any value.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* Status codes. */
+typedef int32_t kda_status_t;
+#define KDA_OK 0
+#define KDA_ERR_INVALID_ARG 1          /* null pointer, negative size, bad stride     */
+#define KDA_ERR_UNSUPPORTED 2          /* dims / chunk size / dtype / interval not built */
+#define KDA_ERR_WORKSPACE_TOO_SMALL 3  /* workspace_bytes below the query's result     */
+#define KDA_ERR_LAUNCH 4               /* hipGetLastError() after the launch            */
+
+/* Element types. */
+typedef int32_t kda_dtype_t;
+#define KDA_F32 0
+#define KDA_BF16 1
+
+/* Flags. */
+#define KDA_FLAG_QK_L2NORM 1u   /* q, k <- x / sqrt(sum x^2 + 1e-6) per (token, head) in-kernel */
+#define KDA_CONV_SILU 1u        /* apply SiLU after the convolution                        */
+
+/* Supported shapes: d_k = d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64}. */
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_string(kda_status_t status);
+
+/*
+ * Bytes of caller-owned scratch that kda_chunk_prefill needs for a call with
+ * these sizes (page "[KK] Prepare B12X Kimi KDA prefill ...", Behavior:
+ * reusable caller-owned scratch).  Depends only on host-known sizes, so one
+ * buffer sized for the largest batch serves every later call.  Returns 0 for
+ * unsupported shapes.
+ */
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                        int32_t num_heads, int32_t dk, int32_t dv,
+                                        int32_t chunk_size);
+
+/*
+ * Chunk prefill over a varlen token batch (page "Add Kimi K3 KDA execution",
+ * KDA execution step 3: build the cumulative gate, then run the chunked
+ * prefill).
+ *
+ *   q, k        [total_tokens, H, dk] of act_dtype, token strides q_stride_t,
+ *               k_stride_t (elements, >= H*dk)
+ *   v           [total_tokens, H, dv] of act_dtype, token stride v_stride_t
+ *   g           [total_tokens, H, dk] fp32, contiguous: per-token log-decay
+ *               (alpha = exp(g), g <= 0 expected).  The kernels factor the
+ *               decay per 16-token sub-chunk; per channel the decay summed
+ *               over any 16 consecutive tokens must stay above -80.
+ *   beta        [total_tokens, H] fp32, contiguous
+ *   cu_seqlens  [num_seqs + 1] int32: sequence i is tokens
+ *               cu_seqlens[i] .. cu_seqlens[i+1]-1.  Empty sequences are
+ *               no-ops (same page, Metadata construction: empty segments).
+ *   state_pool  [num_slots, H, dk, dv] of state_dtype (fp32 or bf16), read
+ *               and written IN PLACE at state_pool[state_indices[i]] -- no
+ *               gather or scatter around the kernels (page "[KK] Prepare B12X
+ *               Kimi KDA prefill ...", Behavior).
+ *   state_indices [num_seqs] int32; < 0 marks a graph-padding sequence: its
+ *               output rows are written as zeros and no state is touched
+ *               (page "Add Kimi K3 KDA execution", KDA execution step 5).
+ *   has_initial_state [num_seqs] uint8 or NULL (= all 1): 0 starts the
+ *               sequence from a zero state, a genuine prompt without state
+ *               (same page, Metadata construction).
+ *   checkpoints [ckpt_capacity, H, dk, dv] of state_dtype or NULL; written
+ *               when ckpt_interval > 0 (page "FlashKDA kernel upgrade supports
+ *               bf16 checkpoint state": checkpoint states stored in the state
+ *               dtype).  Checkpoint j of sequence i is the state after token
+ *               (j+1)*ckpt_interval of this call, stored at row
+ *               sum_{m<i} floor(L_m / ckpt_interval) + j (padding sequences
+ *               keep their rows, unwritten).  Rows >= ckpt_capacity are
+ *               skipped; floor(total_tokens / ckpt_interval) rows always
+ *               suffice.  ckpt_interval must be a multiple of chunk_size.
+ *   scale       output scale (1.0 gives o_t = S_t^T q_t)
+ *   flags       KDA_FLAG_QK_L2NORM
+ *   out         [total_tokens, H, dv] of act_dtype, token stride out_stride_t;
+ *               rows of padding sequences are zeroed, rows outside every
+ *               sequence are left alone.
+ *   workspace   at least kda_chunk_prefill_workspace_size(...) bytes, 256-byte
+ *               aligned.  Its contents are scratch: any call may overwrite it,
+ *               so concurrent calls need separate workspaces.
+ * States are computed in fp32 between chunks; a bf16 state is rounded to
+ * nearest-even when stored (final state and checkpoints).
+ */
+kda_status_t kda_chunk_prefill(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Recurrent decode: one token per row, every non-padding row has a state
+ * (page "Add Kimi K3 KDA execution", KDA execution step 4 and Metadata
+ * construction: a one-token request with an existing state is decode).
+ * Each head's state is streamed once through registers and written back in
+ * place.
+ *
+ *   q, k   [batch, H, dk] of act_dtype, row strides q_stride_b, k_stride_b
+ *   v      [batch, H, dv] of act_dtype, row stride v_stride_b
+ *   g      [batch, H, dk] fp32 contiguous;  beta [batch, H] fp32 contiguous
+ *   state_pool [num_slots, H, dk, dv] of state_dtype, in place
+ *   state_indices [batch] int32; < 0 = padding row (zero output, no state I/O)
+ *   flags  KDA_FLAG_QK_L2NORM
+ *   out    [batch, H, dv] of act_dtype, row stride out_stride_b
+ */
+kda_status_t kda_recurrent_decode(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_b, int64_t k_stride_b, int64_t v_stride_b,
+    const float* g, const float* beta,
+    int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, float scale, uint32_t flags,
+    void* out, int64_t out_stride_b, void* stream);
+
+/*
+ * Gated RMSNorm, norm before gate, on [tokens, heads, dim] rows (page "Add
+ * Kimi K3 KDA execution", What this PR does: output normalisation and gating
+ * with the result in a separate allocation so the input is preserved):
+ *
+ *     y = x / sqrt(mean(x^2) + eps) * weight * silu(gate),  silu(z) = z*sigmoid(z)
+ *
+ * statistics over the `dim` elements of one (token, head).  x, gate, y have
+ * per-token strides (elements) so packed gates can be read in place; heads
+ * of one token are contiguous blocks of `dim`.  weight is [dim] of `dtype` or
+ * NULL (no affine).  Math in fp32; y may not alias x or gate.
+ */
+kda_status_t kda_gated_rmsnorm(
+    const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
+    const void* weight, void* y, int64_t y_stride_t, kda_dtype_t dtype,
+    int64_t tokens, int32_t heads, int32_t dim, float eps, void* stream);
+
+/*
+ * Causal depthwise conv1d over a varlen token batch with a rolling per-slot
+ * conv state (page "Add Kimi K3 KDA execution", KDA execution step 2: run the
+ * causal convolution and update its cache; What this PR does: causal-
+ * convolution state packing).
+ *
+ *     y_t[c] = act( bias[c] + sum_{j<width} weight[c, j] * x_{t-width+1+j}[c] )
+ *
+ * weight[c, width-1] multiplies the current token; inputs before the start of
+ * a sequence come from its conv state (zeros without an initial state).
+ *   x        [total_tokens, channels] of dtype, token stride x_stride_t
+ *   weight   [channels, width] of dtype;  bias [channels] of dtype or NULL
+ *   conv_state_pool [num_slots, width-1, channels] of dtype: row width-2 is
+ *            the most recent input.  After the call it holds the last
+ *            width-1 inputs seen by the sequence (pre-activation).
+ *   state_indices [num_seqs]; < 0 = padding (zero output, no state I/O)
+ *   has_initial_state [num_seqs] uint8 or NULL (= all 1)
+ *   flags    KDA_CONV_SILU
+ *   y        [total_tokens, channels] of dtype, token stride y_stride_t; may
+ *            not alias x.
+ * Supported: width in [2, 8], channels a multiple of 8, dtype bf16 or fp32.
+ */
+kda_status_t kda_causal_conv1d(
+    const void* x, int64_t x_stride_t, const void* weight, const void* bias,
+    void* conv_state_pool, int64_t num_slots,
+    const int32_t* cu_seqlens, const int32_t* state_indices,
+    const uint8_t* has_initial_state, int32_t num_seqs, int64_t total_tokens,
+    int32_t channels, int32_t width, kda_dtype_t dtype, uint32_t flags,
+    void* y, int64_t y_stride_t, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,148 @@
+"""Helpers for the GPU parity tests: run a workload through the C-ABI library
+and through the fp64 oracle, and compare."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from gated_delta_rule_42_amd import workloads as wl
+
+DEV = "cuda"
+
+# Max-abs tolerance by state dtype: fp32 state 1e-2, bf16 state 3e-2 (page
+# "FlashKDA kernel upgrade supports bf16 checkpoint state": the checkpoint
+# correctness test is parametrised as (bf16, 0.03) and (fp32, 0.01)).
+TOL = {torch.float32: 1e-2, torch.bfloat16: 3e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def max_err(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    if a.size == 0:
+        return 0.0
+    d = np.abs(a - b)
+    assert not np.isnan(d).any(), "NaN in comparison"
+    return float(d.max())
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().double().numpy()
+
+
+def gpu_prefill(case: wl.PrefillCase, *, pool: torch.Tensor | None = None, chunk: int | None = None,
+                flags: int | None = None, workspace=None, stream=None):
+    """Runs kda_chunk_prefill; returns (o, pool, checkpoints) on the CPU."""
+    from gated_delta_rule_42_amd import kda
+    q, k, v = case.q.to(DEV), case.k.to(DEV), case.v.to(DEV)
+    g, beta = case.g.to(DEV), case.beta.to(DEV)
+    cu, slots = case.cu_seqlens.to(DEV), case.slots.to(DEV)
+    hi = None if case.has_init is None else case.has_init.to(DEV)
+    p = (case.pool if pool is None else pool).to(DEV).clone()
+    out = torch.full(v.shape, float("nan"), dtype=v.dtype, device=DEV)
+    ck = None
+    if case.ckpt_interval > 0:
+        rows = max(case.ckpt_rows(), 1)
+        ck = torch.full((rows,) + tuple(p.shape[1:]), float("nan"), dtype=p.dtype, device=DEV)
+    if flags is None:
+        flags = kda.KDA_FLAG_QK_L2NORM if case.l2norm_qk else 0
+    kda.chunk_prefill(q, k, v, g, beta, cu, p, slots, out, workspace=workspace,
+                      has_initial_state=hi, checkpoints=ck, ckpt_interval=case.ckpt_interval,
+                      scale=case.scale, chunk_size=chunk or case.chunk_size, flags=flags,
+                      stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu(), p.cpu(), None if ck is None else ck.cpu()
+
+
+def oracle_prefill(case: wl.PrefillCase, heads=None, pool: torch.Tensor | None = None):
+    """fp64 oracle on the same inputs; optionally only the listed heads."""
+    sel = slice(None) if heads is None else list(heads)
+    p = case.pool if pool is None else pool
+    o, pool_out, ck = oracle.prefill(
+        f64(case.q)[:, sel], f64(case.k)[:, sel], f64(case.v)[:, sel], f64(case.g)[:, sel],
+        f64(case.beta)[:, sel], case.cu_seqlens.numpy(), f64(p)[:, sel], case.slots.numpy(),
+        has_init=None if case.has_init is None else case.has_init.numpy(),
+        ckpt_interval=case.ckpt_interval, scale=case.scale, l2norm_qk=case.l2norm_qk)
+    return o, pool_out, ck
+
+
+def token_rows(case: wl.PrefillCase, padding: bool) -> np.ndarray:
+    """Token indices of real (padding=False) or padding (True) sequences."""
+    cu = case.cu_seqlens.tolist()
+    rows = []
+    for i, s in enumerate(case.slots.tolist()):
+        if (s < 0) == padding:
+            rows.extend(range(cu[i], cu[i + 1]))
+    return np.asarray(rows, dtype=np.int64)
+
+
+def check_prefill(case: wl.PrefillCase, got, heads=None, tol=None, label=""):
+    """Compare GPU results with the oracle: o on real rows, zero padding rows,
+    touched slots within tolerance, untouched slots bitwise, checkpoints."""
+    o_g, p_g, ck_g = got
+    tol = TOL[case.pool.dtype] if tol is None else tol
+    o_r, p_r, ck_r = oracle_prefill(case, heads)
+    sel = slice(None) if heads is None else list(heads)
+    real, pad = token_rows(case, False), token_rows(case, True)
+    errs = {}
+    errs["o"] = max_err(f64(o_g)[real][:, sel], o_r[real])
+    if len(pad):
+        assert torch.count_nonzero(o_g[pad]) == 0, f"{label}: padding rows not zero"
+    used = sorted({int(s) for s, L in zip(case.slots.tolist(), case.lengths) if s >= 0 and L > 0})
+    untouched = [s for s in range(case.pool.shape[0]) if s not in used]
+    if used:
+        errs["state"] = max_err(f64(p_g)[used][:, sel], p_r[used])
+    if untouched:
+        assert torch.equal(p_g[untouched].view(torch.int16 if p_g.dtype == torch.bfloat16 else torch.int32),
+                           case.pool[untouched].view(torch.int16 if p_g.dtype == torch.bfloat16 else torch.int32)), \
+            f"{label}: untouched pool slots changed"
+    if case.ckpt_interval > 0 and case.ckpt_rows() > 0:
+        rows_written = []
+        base = 0
+        for s, L in zip(case.slots.tolist(), case.lengths):
+            n = L // case.ckpt_interval
+            if s >= 0:
+                rows_written.extend(range(base, base + n))
+            base += n
+        if rows_written:
+            errs["ckpt"] = max_err(f64(ck_g)[rows_written][:, sel], ck_r[rows_written])
+    say(f"  {label or case.name}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items())
+        + f" (tol {tol:g})")
+    for key, e in errs.items():
+        assert e <= tol, f"{label or case.name}: {key} max-abs error {e:.3e} > {tol}"
+    return errs
+
+
+def gpu_decode(case: wl.DecodeCase, *, pool=None, stream=None):
+    from gated_delta_rule_42_amd import kda
+    q, k, v = case.q.to(DEV), case.k.to(DEV), case.v.to(DEV)
+    g, beta = case.g.to(DEV), case.beta.to(DEV)
+    p = (case.pool if pool is None else pool).to(DEV).clone()
+    out = torch.full(v.shape, float("nan"), dtype=v.dtype, device=DEV)
+    kda.recurrent_decode(q, k, v, g, beta, p, case.slots.to(DEV), out, scale=case.scale,
+                         flags=kda.KDA_FLAG_QK_L2NORM if case.l2norm_qk else 0, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu(), p.cpu()
+
+
+def oracle_decode(case: wl.DecodeCase, pool=None):
+    p = case.pool if pool is None else pool
+    return oracle.decode(f64(case.q), f64(case.k), f64(case.v), f64(case.g), f64(case.beta),
+                         f64(p), case.slots.numpy(), scale=case.scale, l2norm_qk=case.l2norm_qk)
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def inv_sqrt(d: int) -> float:
+    return 1.0 / math.sqrt(d)

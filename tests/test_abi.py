@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/kda.h declares, and rejects bad arguments on the host before any
+launch.  No call here reaches a kernel (every call either fails validation or
+has nothing to do)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_42_amd import build as kbuild
+    srcs = [os.path.join(kbuild.CSRC, s) for s in os.listdir(kbuild.CSRC)] + [HEADER]
+    if (not os.path.exists(kbuild.LIBRARY) or
+            os.path.getmtime(kbuild.LIBRARY) < max(os.path.getmtime(s) for s in srcs)):
+        kbuild.build()
+    from gated_delta_rule_42_amd import kda
+    return kda._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("kda_chunk_prefill", "kda_recurrent_decode", "kda_gated_rmsnorm",
+                 "kda_causal_conv1d", "kda_chunk_prefill_workspace_size",
+                 "kda_abi_version", "kda_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from gated_delta_rule_42_amd import kda
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} not exported"
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings(lib):
+    from gated_delta_rule_42_amd import kda
+    assert kda.abi_version() == 1
+    for code in range(5):
+        assert kda.status_string(code) and kda.status_string(code) != "unknown status"
+    assert kda.status_string(99) == "unknown status"
+
+
+def test_workspace_size(lib):
+    from gated_delta_rule_42_amd import kda
+    one = kda.chunk_prefill_workspace_size(1, 64, 1, 128, 128, 64)
+    assert one > 0 and one % 256 == 0
+    # One record per (chunk slot, head); chunk slots = ceil(T / C) + N.
+    assert kda.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64) == (64 + 1) * 16 * (one // 2)
+    assert kda.chunk_prefill_workspace_size(3, 100, 2, 64, 64, 32) > 0
+    for bad in [(1, 64, 1, 48, 48, 64), (1, 64, 1, 128, 64, 64), (1, 64, 1, 128, 128, 48),
+                (-1, 64, 1, 128, 128, 64), (1, 64, 0, 128, 128, 64)]:
+        assert kda.chunk_prefill_workspace_size(*bad) == 0
+
+
+FAKE = 0x10000   # aligned, never dereferenced: every call below stops in validation
+
+
+def _prefill(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, act=1, qs=2048, ks=2048, vs=2048, g=FAKE, beta=FAKE,
+             cu=FAKE, n=1, T=64, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=4, idx=FAKE,
+             hi=None, ck=None, cap=0, interval=0, scale=1.0, C=64, flags=0, out=FAKE,
+             os=2048, ws=FAKE, wsb=0, stream=None)
+    a.update(over)
+    return lib.kda_chunk_prefill(
+        a["q"], a["k"], a["v"], a["act"], a["qs"], a["ks"], a["vs"], a["g"], a["beta"],
+        a["cu"], a["n"], a["T"], a["H"], a["dk"], a["dv"], a["pool"], a["sdt"], a["slots"],
+        a["idx"], a["hi"], a["ck"], a["cap"], a["interval"], a["scale"], a["C"], a["flags"],
+        a["out"], a["os"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+    assert _prefill(lib, n=0) == K.KDA_OK                              # nothing to do
+    assert _prefill(lib, dk=48, dv=48) == K.KDA_ERR_UNSUPPORTED
+    assert _prefill(lib, dv=64) == K.KDA_ERR_UNSUPPORTED
+    assert _prefill(lib, C=48) == K.KDA_ERR_UNSUPPORTED
+    assert _prefill(lib, interval=100) == K.KDA_ERR_UNSUPPORTED       # not a multiple of C
+    assert _prefill(lib, act=7) == K.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, flags=8) == K.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, q=None) == K.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, cu=None) == K.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, qs=1000) == K.KDA_ERR_INVALID_ARG              # < H * dk
+    assert _prefill(lib, qs=2052) == K.KDA_ERR_INVALID_ARG              # not a multiple of 8
+    assert _prefill(lib, q=FAKE + 2) == K.KDA_ERR_INVALID_ARG           # misaligned
+    assert _prefill(lib, interval=64, cap=4, ck=None) == K.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, T=-1) == K.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, wsb=100) == K.KDA_ERR_WORKSPACE_TOO_SMALL
+    need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
+    assert _prefill(lib, wsb=need, ws=FAKE + 16) == K.KDA_ERR_INVALID_ARG   # 256-B alignment
+
+
+def test_decode_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+
+    def call(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, act=1, qs=2048, ks=2048, vs=2048, g=FAKE, beta=FAKE,
+                 B=4, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=8, idx=FAKE, scale=1.0,
+                 flags=0, out=FAKE, os=2048, stream=None)
+        a.update(over)
+        return lib.kda_recurrent_decode(*a.values())
+
+    assert call(B=0) == K.KDA_OK
+    assert call(dk=96, dv=96) == K.KDA_ERR_UNSUPPORTED
+    assert call(v=None) == K.KDA_ERR_INVALID_ARG
+    assert call(os=100) == K.KDA_ERR_INVALID_ARG
+    assert call(pool=FAKE + 4) == K.KDA_ERR_INVALID_ARG
+    assert call(sdt=3) == K.KDA_ERR_INVALID_ARG
+    assert call(flags=2) == K.KDA_ERR_INVALID_ARG
+
+
+def test_norm_and_conv_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+    n = lambda **o: lib.kda_gated_rmsnorm(*dict(
+        dict(x=FAKE, xs=2048, gate=FAKE, gs=2048, w=None, y=FAKE, ys=2048, dt=1, T=4, H=16,
+             dim=128, eps=1e-6, stream=None), **o).values())
+    assert n(T=0) == K.KDA_OK
+    assert n(dim=100) == K.KDA_ERR_UNSUPPORTED
+    assert n(gate=None) == K.KDA_ERR_INVALID_ARG
+    assert n(eps=-1.0) == K.KDA_ERR_INVALID_ARG
+    assert n(ys=1000) == K.KDA_ERR_INVALID_ARG
+    c = lambda **o: lib.kda_causal_conv1d(*dict(
+        dict(x=FAKE, xs=6144, w=FAKE, b=None, st=FAKE, slots=4, cu=FAKE, idx=FAKE, hi=None,
+             n=1, T=64, C=6144, W=4, dt=1, flags=1, y=FAKE, ys=6144, stream=None), **o).values())
+    assert c(n=0) == K.KDA_OK
+    assert c(W=1) == K.KDA_ERR_UNSUPPORTED
+    assert c(W=9) == K.KDA_ERR_UNSUPPORTED
+    assert c(C=6) == K.KDA_ERR_UNSUPPORTED
+    assert c(w=None) == K.KDA_ERR_INVALID_ARG
+    assert c(xs=100) == K.KDA_ERR_INVALID_ARG
+    assert c(flags=4) == K.KDA_ERR_INVALID_ARG

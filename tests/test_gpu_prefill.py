@@ -1,0 +1,178 @@
+"""Chunk prefill on the GPU against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_42_amd import workloads as wl
+from tests.gpu_support import (TOL, bits, check_prefill, f64, gpu_decode, gpu_prefill, inv_sqrt,
+                               max_err, say)
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+# Lengths spanning: empty, one token, a partial chunk, whole chunks, ragged tails.
+LENS = [0, 1, 17, 64, 100, 130]
+
+
+def _varlen(seed, d, C, state, act=BF16, interval=None, scale=1.0, lens=LENS, H=3,
+            padding=True, has_init=True, **kw):
+    lens = list(lens) + ([23] if padding else [])
+    n = len(lens)
+    slots = list(range(1, 2 * n, 2))[:n]
+    if padding:
+        slots[-1] = -1
+    hi = [1] * n if has_init else None
+    if has_init and n > 2:
+        hi[2] = 0
+    return wl.random_prefill(seed, lens, H, d, d, act_dtype=act, state_dtype=state,
+                             n_slots=2 * n + 1, slots=slots, has_init=hi, chunk_size=C,
+                             ckpt_interval=(2 * C if interval is None else interval),
+                             scale=scale, state_std=0.3, **kw)
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("state", [F32, BF16])
+def test_prefill_parity_small(d, C, state):
+    case = _varlen(1000 + d + C, d, C, state, scale=inv_sqrt(d))
+    check_prefill(case, gpu_prefill(case), label=f"d={d} C={C} state={state}")
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_fp32_activations(C):
+    case = _varlen(77 + C, 64, C, F32, act=F32)
+    check_prefill(case, gpu_prefill(case), label=f"fp32 act C={C}")
+
+
+def test_prefill_l2norm_flag():
+    case = _varlen(5, 128, 64, F32, qk_unit=False, l2norm_qk=True)
+    check_prefill(case, gpu_prefill(case), label="l2norm flag")
+
+
+def test_prefill_tiny_config():
+    """1 sequence, T=64, H=2, d=16, C=16, fp32 everywhere, zero initial state."""
+    case = wl.tiny_prefill()
+    check_prefill(case, gpu_prefill(case), label=case.name)
+
+
+def test_prefill_single_sequence_full_size():
+    """T=4096, H=16, d=128, C=64, bf16 q/k/v, fp32 state from slot 7 of 64."""
+    case = wl.single_seq_prefill()
+    check_prefill(case, gpu_prefill(case), label=case.name)
+
+
+def test_prefill_varlen_full_size():
+    """8 sequences (<=16384 tokens), bf16 256-slot pool, checkpoints every 1024;
+    the oracle checks a sample of heads (heads are independent)."""
+    case = wl.varlen_prefill()
+    check_prefill(case, gpu_prefill(case), heads=[0, 7, 15], label=case.name)
+
+
+def test_prefill_edge_cases():
+    # every sequence empty
+    case = wl.random_prefill(3, [0, 0, 0], 2, 64, 64, n_slots=4, chunk_size=32)
+    o, p, _ = gpu_prefill(case)
+    assert torch.equal(bits(p), bits(case.pool))
+    # single-token sequences with and without a state, one exactly one chunk long
+    case = wl.random_prefill(4, [1, 1, 64, 65], 2, 128, 128, n_slots=6, slots=[5, 0, 2, 3],
+                             has_init=[1, 0, 1, 0], chunk_size=64, state_std=0.3)
+    check_prefill(case, gpu_prefill(case), label="one-token and one-chunk sequences")
+    # only padding
+    case = wl.random_prefill(6, [5, 9], 2, 32, 32, n_slots=3, slots=[-1, -1], chunk_size=16)
+    o, p, _ = gpu_prefill(case)
+    assert torch.count_nonzero(o) == 0 and torch.equal(bits(p), bits(case.pool))
+
+
+def test_prefill_chunk_size_invariance():
+    """The chunked method reaches the same result at every chunk size."""
+    case = _varlen(21, 128, 64, F32, interval=0, padding=False)
+    outs = [gpu_prefill(case, chunk=C) for C in (16, 32, 64)]
+    for o, p, _ in outs[1:]:
+        e = max(max_err(f64(o), f64(outs[0][0])), max_err(f64(p), f64(outs[0][1])))
+        say(f"  chunk-size spread {e:.2e}")
+        assert e <= TOL[F32]
+
+
+def test_prefill_split_calls_carry_state():
+    """One call over 300 tokens equals three calls of 100 through the pool."""
+    case = wl.random_prefill(31, [300], 4, 128, 128, n_slots=3, slots=[1], chunk_size=64,
+                             state_std=0.3)
+    o_full, p_full, _ = gpu_prefill(case)
+    pool = case.pool
+    parts = []
+    for a in range(0, 300, 100):
+        part = wl.PrefillCase("part", case.q[a:a + 100], case.k[a:a + 100], case.v[a:a + 100],
+                              case.g[a:a + 100], case.beta[a:a + 100],
+                              torch.tensor([0, 100], dtype=torch.int32), pool, case.slots, None,
+                              64, 0, 1.0)
+        o, pool, _ = gpu_prefill(part)
+        parts.append(o)
+    e = max(max_err(f64(torch.cat(parts)), f64(o_full)), max_err(f64(pool), f64(p_full)))
+    say(f"  split vs one call {e:.2e}")
+    assert e <= TOL[F32]
+
+
+def test_prefill_routing_is_bit_exact():
+    """Permuting slot assignments and rerunning change no bit of the outputs,
+    states or checkpoints."""
+    case = _varlen(41, 128, 64, BF16, padding=True)
+    a = gpu_prefill(case)
+    b = gpu_prefill(case)
+    for x, y in zip(a, b):
+        assert torch.equal(bits(x), bits(y))
+    n_slots = case.pool.shape[0]
+    perm = torch.randperm(n_slots, generator=torch.Generator().manual_seed(5)).to(torch.int32)
+    pool2 = case.pool.clone()
+    pool2[perm.long()] = case.pool
+    slots2 = torch.where(case.slots >= 0, perm[case.slots.clamp(min=0).long()], case.slots)
+    moved = wl.PrefillCase(case.name, case.q, case.k, case.v, case.g, case.beta,
+                           case.cu_seqlens, pool2, slots2.to(torch.int32), case.has_init,
+                           case.chunk_size, case.ckpt_interval, case.scale)
+    c = gpu_prefill(moved)
+    assert torch.equal(bits(a[0]), bits(c[0]))
+    assert torch.equal(bits(a[1]), bits(c[1][perm.long()]))
+    assert torch.equal(bits(a[2]), bits(c[2]))
+
+
+def test_prefill_workspace_reuse():
+    """A workspace sized for the largest call serves later, smaller calls."""
+    from gated_delta_rule_42_amd import kda
+    big = _varlen(51, 128, 64, F32)
+    small = _varlen(52, 128, 64, F32, lens=[40, 3])
+    ws = torch.empty(kda.chunk_prefill_workspace_size(big.num_seqs, big.total_tokens, 3, 128, 128, 64),
+                     dtype=torch.uint8, device="cuda")
+    check_prefill(big, gpu_prefill(big, workspace=ws), label="workspace first call")
+    check_prefill(small, gpu_prefill(small, workspace=ws), label="workspace reused")
+
+
+def test_decode_equals_one_token_prefill():
+    case = wl.random_decode(61, 40, 4, 128, 128, n_slots=80)
+    o_d, p_d = gpu_decode(case)
+    pre = wl.PrefillCase("as prefill", case.q, case.k, case.v, case.g, case.beta,
+                         torch.arange(41, dtype=torch.int32), case.pool, case.slots, None, 16, 0,
+                         case.scale)
+    o_p, p_p, _ = gpu_prefill(pre)
+    e = max(max_err(f64(o_d), f64(o_p)), max_err(f64(p_d), f64(p_p)))
+    say(f"  decode vs one-token prefill {e:.2e}")
+    assert e <= TOL[F32]
+
+
+def test_prefill_strided_inputs():
+    """q, k, v read in place from a packed [T, 3*H*d] projection; output into a
+    wider buffer."""
+    from gated_delta_rule_42_amd import kda
+    case = wl.random_prefill(71, [70, 33], 4, 64, 64, n_slots=4, chunk_size=32)
+    T, H, d = case.total_tokens, 4, 64
+    packed = torch.cat([case.q.reshape(T, -1), case.k.reshape(T, -1), case.v.reshape(T, -1)], 1).cuda()
+    q = packed[:, :H * d].view(T, H, d)
+    k = packed[:, H * d:2 * H * d].view(T, H, d)
+    v = packed[:, 2 * H * d:].view(T, H, d)
+    wide = torch.zeros(T, 2 * H * d, dtype=torch.bfloat16, device="cuda")
+    out = wide[:, :H * d].view(T, H, d)
+    p = case.pool.cuda().clone()
+    kda.chunk_prefill(q, k, v, case.g.cuda(), case.beta.cuda(), case.cu_seqlens.cuda(), p,
+                      case.slots.cuda(), out, chunk_size=32)
+    torch.cuda.synchronize()
+    o_ref, p_ref, _ = gpu_prefill(case)
+    assert torch.equal(bits(out.cpu()), bits(o_ref)) and torch.equal(bits(p.cpu()), bits(p_ref))
+    assert torch.count_nonzero(wide[:, H * d:]) == 0
