@@ -27,6 +27,38 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+# HBM bytes per launch of each prefill kernel on the T=4096, H=16, d=128 workload,
+# from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) scaled by the
+# same counters' reading for the 1 GiB copy leg.  Each entry is keyed by the
+# sha256 of the kernel source it was taken on; once the source changes the
+# figure no longer describes the kernel and traffic is reported as null.
+_PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
+_DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
+MEASURED_TRAFFIC = {
+    # kernel: (source, its sha256 when measured, bytes read, bytes written)
+    "intra": (_PREFILL_SRC, "d90032e7eb826ce155a3832b3a36f037db8ddc5faa00e165e0b57ac65d5e91c6",
+              88422752, 76022477),
+    "chain": (_PREFILL_SRC, "d90032e7eb826ce155a3832b3a36f037db8ddc5faa00e165e0b57ac65d5e91c6",
+              77311209, 17825792),
+    "decode": (_DECODE_SRC, "793b8b75d03969d4e3dce510735401b11731f26dedb9d9d875c1cf3299173e77",
+               548207217, 538968064),
+}
+
+
+def source_sha256(rel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes(kernel: str):
+    """Measured HBM bytes per launch, or None if not measured on this source."""
+    entry = MEASURED_TRAFFIC.get(kernel)
+    if entry is None or entry[1] != source_sha256(entry[0]):
+        return None
+    return entry[2] + entry[3]
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
@@ -44,20 +76,36 @@ def prefill_alg_flops(T: int, H: int, d: int, C: int) -> float:
     return per_chunk / C * T * H
 
 
+def prefill_stage_alg_bytes(T: int, H: int, dk: int, dv: int, act_bytes: int, state_bytes: int,
+                            n_states: int) -> dict:
+    """The same algorithmic bytes split by the kernel that must move them: the
+    intra-chunk kernel reads q, k, v, g and beta; the chain kernel reads and
+    writes the states and writes o.  The workspace records passed from one to
+    the other are an artefact of the split, not algorithmic traffic."""
+    intra = T * H * ((2 * dk + dv) * act_bytes + 4 * dk + 4)
+    chain = T * H * dv * act_bytes + 2 * n_states * H * dk * dv * state_bytes
+    return {"intra": intra, "chain": chain}
+
+
 def decode_alg_bytes(B: int, H: int, dk: int, dv: int, act_bytes: int, state_bytes: int) -> int:
     per_seq_head = 2 * dk * dv * state_bytes + (2 * dk + 2 * dv) * act_bytes + 4 * dk + 4
     return B * H * per_seq_head
 
 
-def time_calls(fn, steps: int, warmup: int):
+def time_calls(fn, steps: int, warmup: int, per_kernel: bool = False):
     """Warm up, then time exactly `steps` calls with HIP events on the current
-    stream (the stream the kernels run on), bracketed by synchronize."""
+    stream (the stream the kernels run on), bracketed by synchronize.  With
+    per_kernel, the library's prefill timing session also records events
+    around each of its two kernels inside the same timed region."""
     import torch
+    from gated_delta_rule_42_amd import kda
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if per_kernel:
+        kda.prefill_timing_begin(steps)
     w0 = time.perf_counter()
     e0.record()
     for i in range(steps):
@@ -65,7 +113,11 @@ def time_calls(fn, steps: int, warmup: int):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    return e0.elapsed_time(e1) / steps, wall
+    stages = None
+    if per_kernel:
+        intra_ms, chain_ms, n = kda.prefill_timing_end()
+        stages = {"intra": intra_ms / n, "chain": chain_ms / n}
+    return e0.elapsed_time(e1) / steps, wall, stages
 
 
 def bench_prefill(steps: int, warmup: int):
@@ -90,8 +142,8 @@ def bench_prefill(steps: int, warmup: int):
         q, k, v, g, beta = sets[i % n_sets]
         kda.chunk_prefill(q, k, v, g, beta, cu, pool, slots, out, workspace=ws, chunk_size=64)
 
-    ms, wall = time_calls(call, steps, warmup)
-    return case, ms, wall
+    ms, wall, stages = time_calls(call, steps, warmup, per_kernel=True)
+    return case, ms, wall, stages
 
 
 def bench_decode(steps: int, warmup: int):
@@ -107,7 +159,7 @@ def bench_decode(steps: int, warmup: int):
     def call(i):
         kda.recurrent_decode(q, k, v, g, beta, pool, slots, out)
 
-    ms, wall = time_calls(call, steps, warmup)
+    ms, wall, _ = time_calls(call, steps, warmup)
     return case, ms, wall
 
 
@@ -142,8 +194,20 @@ def bench_pipeline(steps: int, warmup: int):
                           flags=kda.KDA_FLAG_QK_L2NORM)
         kda.gated_rmsnorm(o, gate, z, weight=nw, eps=lc.eps)
 
-    ms, wall = time_calls(call, steps, warmup)
+    ms, wall, _ = time_calls(call, steps, warmup)
     return lc, ms, wall
+
+
+def bench_copy(steps: int, warmup: int, nbytes: int = 1 << 30):
+    """A plain device-to-device copy of known size (torch's copy kernel): the
+    calibration point for the HBM byte counters and the achievable-bandwidth
+    reference."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms, wall, _ = time_calls(lambda i: dst.copy_(src), steps, warmup)
+    return {"value": 2 * nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s (read + write)",
+            "ms_per_step": ms, "steps": steps, "bytes_read": nbytes, "bytes_written": nbytes}
 
 
 def cpu_baseline(case, budget_s: float = 10.0):
@@ -174,7 +238,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "pipeline"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "pipeline", "copy"], default=None,
                     help="run one leg only (for profiling); prints that leg's numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -190,11 +254,14 @@ def main() -> int:
     K, W = args.steps, args.warmup
     result = {}
     if args.only in (None, "prefill"):
-        case, ms, wall = bench_prefill(K, W)
+        case, ms, wall, stages = bench_prefill(K, W)
         T, H, d = 4096, 16, 128
         nbytes = prefill_alg_bytes(T, H, d, d, 2, 4, 1)
+        stage_bytes = prefill_stage_alg_bytes(T, H, d, d, 2, 4, 1)
         flops = prefill_alg_flops(T, H, d, 64)
         gbs = nbytes / (ms * 1e-3) / 1e9
+        dom = max(stages, key=stages.get)
+        dom_gbs = stage_bytes[dom] / (stages[dom] * 1e-3) / 1e9
         result.update({
             "metric": "KDA prefill tokens/s (T=4096,H=16,d=128) + decode seq/s; % MFMA/HBM roofline",
             "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -203,11 +270,16 @@ def main() -> int:
             "config": {"workload": case.name, "seqs": 1, "seq_len": T, "heads": H, "d_k": d,
                        "d_v": d, "chunk": 64, "act": "bf16", "g_beta": "fp32",
                        "state": "fp32 pool[64] slot 7", "parallelism": "none (1 GPU)"},
-            "roofline": {"kernel": "kda_chunk_prefill (intra_kernel + chain_kernel)",
-                         "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                         "alg_bytes": nbytes, "alg_flops": flops,
-                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+            "roofline": {"kernel": f"{dom}_kernel", "bound": "hbm", "achieved": dom_gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
+                         "traffic": traffic_bytes(dom), "alg_bytes": stage_bytes[dom],
+                         "ms_per_launch": stages[dom],
+                         "stage_ms": stages},
+            "call_roofline": {"kernels": "intra_kernel + chain_kernel", "bound": "hbm",
+                              "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": gbs / HBM_PEAK_GBS, "alg_bytes": nbytes,
+                              "alg_flops": flops,
+                              "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         })
     if args.only in (None, "decode"):
         dcase, dms, dwall = bench_decode(K, W)
@@ -219,12 +291,14 @@ def main() -> int:
             "workload": dcase.name,
             "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": dgbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                         "traffic": None, "alg_bytes": dbytes}}
+                         "traffic": traffic_bytes("decode"), "alg_bytes": dbytes}}
     if args.only in (None, "pipeline"):
         lc, pms, pwall = bench_pipeline(K, W)
         result["pipeline"] = {
             "value": lc.T_call / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms,
             "steps": K, "workload": lc.name + " (one 4096-token call per step)"}
+    if args.only == "copy":
+        result["copy"] = bench_copy(K, W)
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)
     if args.only is not None and "value" not in result:

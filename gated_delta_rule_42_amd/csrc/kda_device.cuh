@@ -69,6 +69,28 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane)
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, then synchronises the waves.  Unlike __syncthreads() it does not
+// wait for outstanding global loads (including asynchronous loads into LDS
+// buffers that the barrier does not protect), so prefetches stay in flight.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations issued by this wave are
+// outstanding (they complete in issue order).  gfx9 encoding of s_waitcnt:
+// vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] left at
+// their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
 // MFMA wrappers.
 //
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].

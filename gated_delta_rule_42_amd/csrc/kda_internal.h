@@ -36,6 +36,10 @@ struct PrefillArgs {
     void* out; int64_t out_stride;
     void* workspace;
     kda_dtype_t act, state;
+    // Optional timing events (all null, or all valid): recorded on the stream
+    // before the intra-chunk kernel, between it and the chain kernel, and
+    // after the chain kernel.
+    hipEvent_t ev[3];
 };
 // Workspace bytes for a call; 0 if the shape is unsupported.
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t heads,

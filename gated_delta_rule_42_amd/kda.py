@@ -64,6 +64,11 @@ def _load() -> ctypes.CDLL:
     lib.kda_causal_conv1d.restype = i32
     lib.kda_causal_conv1d.argtypes = [
         vp, i64, vp, vp, vp, i64, vp, vp, vp, i32, i64, i32, i32, i32, u32, vp, i64, vp]
+    lib.kda_prefill_timing_begin.restype = i32
+    lib.kda_prefill_timing_begin.argtypes = [i32]
+    lib.kda_prefill_timing_end.restype = i32
+    lib.kda_prefill_timing_end.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                           ctypes.POINTER(ctypes.c_int32)]
     return lib
 
 
@@ -216,3 +221,18 @@ def causal_conv1d(x, weight, cu_seqlens, conv_state_pool, state_indices, y, *, b
         _ptr(has_initial_state), state_indices.numel(), T, C, W, _dtype(x),
         KDA_CONV_SILU if silu else 0, _ptr(y), y.stride(0), _stream(stream))
     _check("kda_causal_conv1d", status)
+
+
+def prefill_timing_begin(max_calls: int) -> None:
+    """kda_prefill_timing_begin: time the two kernels of the next `max_calls`
+    chunk_prefill calls with HIP events on their stream."""
+    _check("kda_prefill_timing_begin", _lib.kda_prefill_timing_begin(int(max_calls)))
+
+
+def prefill_timing_end() -> tuple[float, float, int]:
+    """kda_prefill_timing_end: (intra-chunk ms, chain ms) summed over the timed
+    calls, and the number of calls timed."""
+    ms = (ctypes.c_float * 2)()
+    n = ctypes.c_int32(0)
+    _check("kda_prefill_timing_end", _lib.kda_prefill_timing_end(ms, ctypes.byref(n)))
+    return float(ms[0]), float(ms[1]), int(n.value)

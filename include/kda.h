@@ -15,8 +15,9 @@
  *
  * Conventions for every entry point
  *   - Every pointer argument is DEVICE memory owned by the caller, except
- *     where a comment says otherwise.  The library allocates nothing, keeps no
- *     state between calls and never synchronises: each call only enqueues
+ *     where a comment says otherwise.  Apart from the optional timing aid at the
+ *     end of this header, the library allocates nothing, keeps no state
+ *     between calls and never synchronises: each call only enqueues
  *     kernels on `stream` (a hipStream_t; NULL = the null stream), so it can
  *     be captured into a HIP graph.  Outputs are valid once the stream has
  *     reached that point.
@@ -214,6 +215,26 @@ kda_status_t kda_causal_conv1d(
     const uint8_t* has_initial_state, int32_t num_seqs, int64_t total_tokens,
     int32_t channels, int32_t width, kda_dtype_t dtype, uint32_t flags,
     void* y, int64_t y_stride_t, void* stream);
+
+/*
+ * Per-kernel timing of kda_chunk_prefill (a benchmarking aid; not part of the
+ * operator).  The prefill is two kernels on the call's stream: the
+ * intra-chunk kernel (every chunk in parallel) and the chain kernel (the
+ * chunk-to-chunk state recurrence).  Between kda_prefill_timing_begin and
+ * kda_prefill_timing_end, each kda_chunk_prefill call, up to max_calls of
+ * them, records one HIP event on its stream before the intra-chunk kernel,
+ * one between the two kernels and one after the chain kernel.
+ *
+ * This is the library's only host-side state and its only allocation: begin
+ * creates 3 * max_calls HIP events; end waits for the recorded ones, writes the
+ * summed durations in milliseconds (stage_ms[0] intra-chunk, stage_ms[1]
+ * chain) and the number of timed calls, and destroys the events.  Calls beyond
+ * max_calls run untimed.  Not thread-safe; at most one session at a time
+ * (begin while a session is open returns KDA_ERR_INVALID_ARG).  The event
+ * records add a small gap between the two kernels of a timed call.
+ */
+kda_status_t kda_prefill_timing_begin(int32_t max_calls);
+kda_status_t kda_prefill_timing_end(float* stage_ms, int32_t* calls);
 
 #ifdef __cplusplus
 }
