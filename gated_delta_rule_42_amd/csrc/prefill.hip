@@ -159,10 +159,81 @@ __device__ __forceinline__ bf16x4 pack_bf16x4(const f32x4& x)
     return r;
 }
 
+// Element offset of (row, col) in a row-major bf16 tile with ROWLEN elements
+// per row whose 16-byte chunks are permuted within each row by an XOR of the
+// row index.  16 lanes reading the same logical chunk of 16 consecutive rows
+// then touch 16 distinct bank groups whether the LDS has 32 or 64 banks.  The
+// workspace records are written in this layout and copied byte for byte into
+// LDS.
+template <int ROWLEN>
+__device__ __forceinline__ int swz(int row, int col)
+{
+    constexpr int NC = ROWLEN / 8;                 // 16-byte chunks per row
+    static_assert(NC == 4 || NC == 8 || NC == 16, "row length");
+    int f;
+    if constexpr (NC == 16) f = row & 15;
+    else if constexpr (NC == 8) f = (row & 7) ^ ((row >> 3) & 1);
+    else f = (row >> 2) & 3;
+    return row * ROWLEN + (((col >> 3) ^ f) << 3) + (col & 7);
+}
+
+// ---------------------------------------------------------------------------
+// Lane-level helpers for the MFMA operand layouts (16x16x32 bf16): an
+// "A fragment" of a 16-row tile holds, in lane l, row l % 16 and the 8
+// consecutive K-elements 8 * (l / 16) .. + 7 of one 32-wide K block.
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16r..16r+15).
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_scan16(float x)
+{
+    x += dpp_row_shr<1>(x);
+    x += dpp_row_shr<2>(x);
+    x += dpp_row_shr<4>(x);
+    x += dpp_row_shr<8>(x);
+    return x;
+}
+
+// B operands of the identity products that transpose an A fragment: with
+// B = E_half (the 32x16 matrix with ones at (n + 16 * half, n)), the product
+// A[16x32] * E_half is columns 16*half .. 16*half+15 of A, returned in the
+// accumulator layout (lane l: column l % 16, rows 4 * (l / 16) .. + 3).  The
+// products are exact: every output is one bf16 value times 1 plus zeros.
+__device__ __forceinline__ bf16x8 identity_half(int half, int lane)
+{
+    const int e = (lane & 15) + 16 * half - 8 * (lane >> 4);
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = static_cast<bf16>(i == e ? 1.0f : 0.0f);
+    return b;
+}
+
 // ---------------------------------------------------------------------------
 // intra_kernel: everything in a chunk that does not depend on the state.
-// Phase 0 stages the chunk's q, k, v, g, beta into LDS with every global
-// load issued before the first use; all later phases read LDS only.
+//
+// Wave w < NS owns token tile w (tokens 16w .. 16w+15).  Each lane keeps one
+// token's q, k, v, g as A fragments (8 consecutive channels per 32-channel
+// block) for the whole kernel, so the elementwise work happens in registers:
+//   1. gate cumsum: a DPP scan over the tile's 16 lanes, plus the totals of
+//      the tiles before (LDS).
+//   2. decay factors relative to the tile's reference point b_w (the token
+//      before the tile): f_w = e^{G_r - G_{b_w}} <= 1, and for earlier
+//      reference points f_j = f_w * prod_{j<=m<w} e^{tile total m}, products
+//      of factors <= 1 (no exponential of a positive number).  Q~ and K~ use
+//      f_0; the Gram blocks (w, j) use f_j on this tile's rows and
+//      K^_s = k_s e^{G_{b_j} - G_s} (written by wave j) on the other side.
+//   3. Gram blocks on bf16 MFMA, computed transposed so each lane holds 4
+//      consecutive columns of one row: M (to LDS, fp32) and Aqk (record).
+//   4. X = (I + M)^{-1}: forward substitution on each 16x16 diagonal block
+//      (one lane per column), then the off-diagonal blocks row by row on
+//      fp32 MFMA.  T = X Diag(beta) in bf16.
+//   5. W = T K~ and U = T V on bf16 MFMA from LDS tiles, K~^T and V^T having
+//      been transposed with identity MFMA products in step 2.
+// Record stores are 8- or 16-byte vector stores in the swizzled layout.
 template <int D, int BT, typename AT>
 __global__ __launch_bounds__(kThreads)
 void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* __restrict__ v,
@@ -172,25 +243,24 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                   uint8_t* __restrict__ ws)
 {
     using P = Shape<D, BT>;
-    constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS;
-    constexpr int GP = D + 4;                // fp32 pitch of sG (16-B rows)
-    constexpr int RP = D + 8;                // bf16 pitch of sQ / sK
-    constexpr int MP = BT + 4;               // fp32 pitch of sM / sX
-    constexpr int TP = BTP + 8;              // bf16 pitch of the transposed tiles
-    constexpr int VG = D / 8;                // 8-element groups per activation row
+    constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NKK = P::NKK_K;
+    constexpr int XP = BT + 4;               // fp32 pitch of the X / M tiles
+    constexpr int TP = BTP + 8;              // bf16 pitch of the token-contiguous tiles
 
-    __shared__ __attribute__((aligned(16))) float sG[BT][GP];    // g, then its inclusive cumsum
-    __shared__ __attribute__((aligned(16))) bf16 sQ[BT][RP];     // raw q
-    __shared__ __attribute__((aligned(16))) bf16 sK[BT][RP];     // raw k
-    __shared__ __attribute__((aligned(16))) bf16 sVt[D][TP];     // V^T
-    __shared__ __attribute__((aligned(16))) float sM[BT][MP];    // strict_lower(Diag(beta) K~ K^T)
-    __shared__ __attribute__((aligned(16))) float sX[BT][MP];    // (I + M)^{-1}
-    __shared__ __attribute__((aligned(16))) bf16 sKt[DKP][TP];   // K~^T
-    __shared__ float sRq[BT], sRk[BT], sBeta[BT];
-    __shared__ float sTmp[4][16][17];        // per-wave 16x16 scratch for the solve
+    __shared__ __attribute__((aligned(16))) float sTot[4][DKP];          // tile totals of g
+    __shared__ __attribute__((aligned(16))) float sE[4][DKP];            // e^{tile total}
+    __shared__ __attribute__((aligned(16))) bf16x8 sKh[NS][NKK][kWave];  // K^ fragments
+    __shared__ __attribute__((aligned(16))) float sM[BT][XP];            // strict_lower(Diag(beta) K~ K^T)
+    __shared__ __attribute__((aligned(16))) float sX[BT][XP];            // X
+    __shared__ __attribute__((aligned(16))) float sXt[BT][XP];           // X^T
+    __shared__ __attribute__((aligned(16))) bf16 sT[BT][TP];             // T = X Diag(beta)
+    __shared__ __attribute__((aligned(16))) bf16 sKt[DKP][TP];           // K~^T
+    __shared__ __attribute__((aligned(16))) bf16 sVt[DKP][TP];           // V^T
+    __shared__ __attribute__((aligned(16))) float sBeta[BTP];
 
     const int x = blockIdx.x, h = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, g4 = lane >> 4;
 
     int seq = 0, first = 0;
@@ -207,288 +277,275 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     bf16* wA = reinterpret_cast<bf16*>(rec) + P::OFF_A;
     float* wEg = reinterpret_cast<float*>(rec + P::EG_BYTE_OFF);
 
-    // 0. Stage q, k, v (as bf16), g and beta.
-    {
-        constexpr int NQ = (BT * VG + kThreads - 1) / kThreads;
-        constexpr int NG = (BT * (D / 4) + kThreads - 1) / kThreads;
-        bf16x8 rq[NQ], rk[NQ], rv[NQ];
-        float4 rg[NG];
-#pragma unroll
-        for (int it = 0; it < NQ; ++it) {
-            const int idx = tid + it * kThreads;
-            const int r = idx / VG, c0 = 8 * (idx % VG);
-            if (idx < BT * VG && r < len) {
-                const int64_t t = t0 + r;
-                rq[it] = load8_bf16(q + t * qs + (int64_t)h * D + c0);
-                rk[it] = load8_bf16(k + t * ks + (int64_t)h * D + c0);
-                rv[it] = load8_bf16(v + t * vs + (int64_t)h * D + c0);
-            } else {
-                rq[it] = bf16x8{}; rk[it] = bf16x8{}; rv[it] = bf16x8{};
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < NG; ++it) {
-            const int idx = tid + it * kThreads;
-            const int r = idx / (D / 4), c0 = 4 * (idx % (D / 4));
-            rg[it] = (idx < BT * (D / 4) && r < len)
-                         ? *reinterpret_cast<const float4*>(g + ((t0 + r) * heads + h) * D + c0)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (tid < BT) sBeta[tid] = tid < len ? beta[(t0 + tid) * heads + h] : 0.0f;
-#pragma unroll
-        for (int it = 0; it < NQ; ++it) {
-            const int idx = tid + it * kThreads;
-            if (idx < BT * VG) {
-                const int r = idx / VG, c0 = 8 * (idx % VG);
-                *reinterpret_cast<bf16x8*>(&sQ[r][c0]) = rq[it];
-                *reinterpret_cast<bf16x8*>(&sK[r][c0]) = rk[it];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sVt[c0 + e][r] = rv[it][e];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < NG; ++it) {
-            const int idx = tid + it * kThreads;
-            if (idx < BT * (D / 4))
-                *reinterpret_cast<float4*>(&sG[idx / (D / 4)][4 * (idx % (D / 4))]) = rg[it];
-        }
-        if (BTP > BT)
-            for (int idx = tid; idx < D * (BTP - BT); idx += kThreads)
-                sVt[idx / (BTP - BT)][BT + idx % (BTP - BT)] = static_cast<bf16>(0.0f);
-    }
-    __syncthreads();
+    const bool tok_wave = wave < NS;
+    const int r = 16 * (tok_wave ? wave : 0) + l16;  // this lane's token row
+    const bool valid = tok_wave && r < len;
 
-    // 1. Inclusive cumulative gate per channel: NSPLIT threads per channel
-    //    scan consecutive row segments, then add the totals before them.
-    {
-        constexpr int NSPLIT = kThreads / D;
-        constexpr int RPC = BT / NSPLIT;
-        static_assert(RPC >= 1 && BT % NSPLIT == 0, "gate split");
-        const int c = tid % D, part = tid / D;
-        float acc = 0.0f;
+    // 0. Loads: this lane's token, channels 32 kk + 8 g4 .. + 7.
+    bf16x8 kq[NKK], kk8[NKK], kv[NKK];
+    float gv[NKK][8];
+    float b_r = 0.0f;
 #pragma unroll
-        for (int i = 0; i < RPC; ++i) {
-            acc += sG[part * RPC + i][c];
-            sG[part * RPC + i][c] = acc;
+    for (int kk = 0; kk < NKK; ++kk) {
+        const int c0 = 32 * kk + 8 * g4;
+        if (valid && c0 < D) {
+            const int64_t t = t0 + r;
+            kq[kk] = load8_bf16(q + t * qs + (int64_t)h * D + c0);
+            kk8[kk] = load8_bf16(k + t * ks + (int64_t)h * D + c0);
+            kv[kk] = load8_bf16(v + t * vs + (int64_t)h * D + c0);
+            load8(g + (t * heads + h) * D + c0, gv[kk]);
+        } else {
+            kq[kk] = bf16x8{}; kk8[kk] = bf16x8{}; kv[kk] = bf16x8{};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[kk][e] = 0.0f;
         }
-        __syncthreads();
-        float pre = 0.0f;
-        for (int p = 0; p < part; ++p) pre += sG[(p + 1) * RPC - 1][c];
-        __syncthreads();
-        if (part > 0)
-#pragma unroll
-            for (int i = 0; i < RPC; ++i) sG[part * RPC + i][c] += pre;
     }
-    // Row norms for the optional q/k L2 normalisation.
-    {
-        constexpr int TPRN = kThreads / BT;
-        const int r = tid / TPRN, part = tid % TPRN;
+    if (valid) b_r = beta[(t0 + r) * heads + h];
+    if (tok_wave && g4 == 0) sBeta[r] = b_r;
+    if (BTP > BT && tid < BTP - BT) sBeta[BT + tid] = 0.0f;
+
+    // 1. Cumulative gate inside the tile (DPP scan over the 16 token lanes).
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[kk][e] = row_scan16(gv[kk][e]);
+    if (tok_wave && l16 == 15) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int c0 = 32 * kk + 8 * g4;
+            *reinterpret_cast<float4*>(&sTot[wave][c0]) = make_float4(gv[kk][0], gv[kk][1], gv[kk][2], gv[kk][3]);
+            *reinterpret_cast<float4*>(&sTot[wave][c0 + 4]) = make_float4(gv[kk][4], gv[kk][5], gv[kk][6], gv[kk][7]);
+        }
+    }
+    // L2 norms of q and k over the token's channels (4 lanes share a token).
+    float rq = 1.0f, rk = 1.0f;
+    if (flags & KDA_FLAG_QK_L2NORM) {
         float sq = 0.0f, sk = 0.0f;
-        if (flags & KDA_FLAG_QK_L2NORM) {
-            for (int c = part; c < D; c += TPRN) {
-                const float a = static_cast<float>(sQ[r][c]), b = static_cast<float>(sK[r][c]);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = static_cast<float>(kq[kk][e]), b = static_cast<float>(kk8[kk][e]);
                 sq += a * a;
                 sk += b * b;
             }
-        }
-#pragma unroll
-        for (int off = TPRN / 2; off > 0; off >>= 1) {
-            sq += __shfl_xor(sq, off, kWave);
-            sk += __shfl_xor(sk, off, kWave);
-        }
-        if (part == 0) {
-            const bool nrm = (flags & KDA_FLAG_QK_L2NORM) != 0;
-            sRq[r] = nrm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-            sRk[r] = nrm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-        }
+        sq += __shfl_xor(sq, 16, kWave); sq += __shfl_xor(sq, 32, kWave);
+        sk += __shfl_xor(sk, 16, kWave); sk += __shfl_xor(sk, 32, kWave);
+        rq = 1.0f / sqrtf(sq + 1e-6f);
+        rk = 1.0f / sqrtf(sk + 1e-6f);
     }
     __syncthreads();
 
-    // 2. Elementwise factors.  Q~ -> record (row-major); K~^T -> LDS and
-    //    Kb^T -> record (8 consecutive tokens per thread, 16-B stores).
-    for (int idx = tid; idx < BT * (DKP / 8); idx += kThreads) {
-        const int r = idx / (DKP / 8), c0 = 8 * (idx % (DKP / 8));
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (r < len && c0 < D) {
+    // Tile exponentials and the chunk's total decay.
+    for (int idx = tid; idx < NS * DKP; idx += kThreads)
+        sE[idx / DKP][idx % DKP] = __expf(sTot[idx / DKP][idx % DKP]);
+    for (int c = tid; c < DKP; c += kThreads) {
+        float tot = 0.0f;
+        for (int j = 0; j < NS; ++j) tot += sTot[j][c];
+        wEg[c] = c < D ? __expf(tot) : 0.0f;
+    }
+    // The scan is relative to the tile's reference point: gv = G_r - G_{b_w}.
+    float fw[NKK][8];                         // e^{G_r - G_{b_w}}
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[e] = static_cast<float>(sQ[r][c0 + e]) * sRq[r] * __expf(sG[r][c0 + e]);
-        }
-        *reinterpret_cast<bf16x8*>(wQ + (int64_t)r * DKP + c0) = pack_bf16x8(o);
-    }
-    for (int idx = tid; idx < DKP * (BTP / 8); idx += kThreads) {
-        const int c = idx / (BTP / 8), s0 = 8 * (idx % (BTP / 8));
-        float kt[8], kb[8];
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s = s0 + e;
-            kt[e] = 0.0f;
-            kb[e] = 0.0f;
-            if (s < len && c < D) {
-                const float kv = static_cast<float>(sK[s][c]) * sRk[s];
-                kt[e] = kv * __expf(sG[s][c]);
-                kb[e] = kv * __expf(sG[BT - 1][c] - sG[s][c]);
-            }
-        }
-        *reinterpret_cast<bf16x8*>(&sKt[c][s0]) = pack_bf16x8(kt);
-        *reinterpret_cast<bf16x8*>(wKb + (int64_t)c * BTP + s0) = pack_bf16x8(kb);
-    }
-    for (int c = tid; c < DKP; c += kThreads) wEg[c] = c < D ? __expf(sG[BT - 1][c]) : 0.0f;
-    // Zero the blocks above the diagonal of M and X, and of Aqk (with its
-    // token padding).
-    for (int idx = tid; idx < BT * BT; idx += kThreads) {
-        const int r = idx / BT, s = idx % BT;
-        if (s >= 16 * (r / 16 + 1)) { sM[r][s] = 0.0f; sX[r][s] = 0.0f; }
-    }
-    for (int idx = tid; idx < BT * (BTP / 8); idx += kThreads) {
-        const int r = idx / (BTP / 8), s0 = 8 * (idx % (BTP / 8));
-        if (s0 >= 16 * (r / 16 + 1)) *reinterpret_cast<bf16x8*>(wA + (int64_t)r * BTP + s0) = bf16x8{};
-    }
+        for (int e = 0; e < 8; ++e) fw[kk][e] = __expf(gv[kk][e]);
+    __syncthreads();                          // sE ready
 
-    // 3. Gram blocks on bf16 MFMA (K = key dim), computed transposed so each
-    //    lane ends up with 4 consecutive columns s of one row r:
-    //    C[s][r] = (e^{G_b - G_s} k_s) . (e^{G_r - G_b} k_r or q_r), b = the
-    //    token before sub-chunk i.  Wave w owns block row i = w.
-    if (wave < NS) {
-        const int i = wave;
-        const int r = 16 * i + l16;
-        bf16x8 bK[P::NKK_K], bQ[P::NKK_K];
+    // 2. Factors.  For this tile (reference b_w):
+    //    K^ = k / f_w -> LDS (Gram A side); Kb = K^ * prod_{m>=w} E_m -> record;
+    //    f_0 = f_w * prod_{m<w} E_m: Q~ = q f_0 -> record, K~ = k f_0 -> LDS (transposed).
+    if (tok_wave) {
+        const bf16x8 id0 = identity_half(0, lane), id1 = identity_half(1, lane);
 #pragma unroll
-        for (int kk = 0; kk < P::NKK_K; ++kk) {
+        for (int kk = 0; kk < NKK; ++kk) {
             const int c0 = 32 * kk + 8 * g4;
-            float fk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            float fq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (r < len && c0 < D) {
+            float before[8], after[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { before[e] = 1.0f; after[e] = 1.0f; }
+            for (int m = 0; m < NS; ++m) {
+                const float4 a = *reinterpret_cast<const float4*>(&sE[m][c0]);
+                const float4 b = *reinterpret_cast<const float4*>(&sE[m][c0 + 4]);
+                const float em[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float gb = i > 0 ? sG[16 * i - 1][c0 + e] : 0.0f;
-                    const float ex = __expf(sG[r][c0 + e] - gb);
-                    fk[e] = static_cast<float>(sK[r][c0 + e]) * sRk[r] * ex;
-                    fq[e] = static_cast<float>(sQ[r][c0 + e]) * sRq[r] * ex;
+                    if (m < wave) before[e] *= em[e];
+                    else after[e] *= em[e];
                 }
             }
-            bK[kk] = pack_bf16x8(fk);
-            bQ[kk] = pack_bf16x8(fq);
+            float kh[8], kb[8], qt[8], kt[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kn = static_cast<float>(kk8[kk][e]) * rk;
+                const float inv = __builtin_amdgcn_rcpf(fw[kk][e]);
+                const float f0 = fw[kk][e] * before[e];
+                kh[e] = kn * inv;
+                kb[e] = kh[e] * after[e];
+                qt[e] = static_cast<float>(kq[kk][e]) * rq * f0;
+                kt[e] = kn * f0;
+            }
+            sKh[wave][kk][lane] = pack_bf16x8(kh);
+            *reinterpret_cast<bf16x8*>(wQ + swz<DKP>(r, c0)) = pack_bf16x8(qt);
+            // Transposes through the identity products: lane l gets channel
+            // 32 kk + 16 half + l % 16, tokens 16 w + 4 (l / 16) .. + 3.
+            const bf16x8 akb = pack_bf16x8(kb), akt = pack_bf16x8(kt);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int c = 32 * kk + 16 * half + l16;
+                const bf16x8 id = half ? id1 : id0;
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 tb = mfma16x16x32(akb, id, zero);
+                const f32x4 tk = mfma16x16x32(akt, id, zero);
+                const f32x4 tv = mfma16x16x32(kv[kk], id, zero);
+                *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(c, 16 * wave + 4 * g4)) = pack_bf16x4(tb);
+                *reinterpret_cast<bf16x4*>(&sKt[c][16 * wave + 4 * g4]) = pack_bf16x4(tk);
+                *reinterpret_cast<bf16x4*>(&sVt[c][16 * wave + 4 * g4]) = pack_bf16x4(tv);
+            }
         }
-        for (int j = 0; j <= i; ++j) {
-            const int s = 16 * j + l16;
-            f32x4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+    }
+    if (BTP > BT) {                           // token padding of the transposed tiles
+        for (int idx = tid; idx < DKP * (BTP - BT) / 4; idx += kThreads) {
+            const int c = idx / ((BTP - BT) / 4), s = BT + 4 * (idx % ((BTP - BT) / 4));
+            *reinterpret_cast<bf16x4*>(&sKt[c][s]) = bf16x4{};
+            *reinterpret_cast<bf16x4*>(&sVt[c][s]) = bf16x4{};
+            *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(c, s)) = bf16x4{};
+        }
+    }
+    __syncthreads();                          // sKh, sKt, sVt ready
+
+    // 3. Gram blocks (w, j), j <= w:  C[s][r] = K^_s . (f_j k_r)  and  K^_s . (f_j q_r).
+    if (tok_wave) {
+        float fj[NKK][8];
 #pragma unroll
-            for (int kk = 0; kk < P::NKK_K; ++kk) {
-                const int c0 = 32 * kk + 8 * g4;
-                float fa[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (s < len && c0 < D) {
+        for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float gb = i > 0 ? sG[16 * i - 1][c0 + e] : 0.0f;
-                        fa[e] = static_cast<float>(sK[s][c0 + e]) * sRk[s] * __expf(gb - sG[s][c0 + e]);
-                    }
+            for (int e = 0; e < 8; ++e) fj[kk][e] = fw[kk][e];
+        for (int j = wave; j >= 0; --j) {
+            if (j < wave) {                   // f_j = f_{j+1} * E_j
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int c0 = 32 * kk + 8 * g4;
+                    const float4 a = *reinterpret_cast<const float4*>(&sE[j][c0]);
+                    const float4 b = *reinterpret_cast<const float4*>(&sE[j][c0 + 4]);
+                    const float em[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) fj[kk][e] *= em[e];
                 }
-                const bf16x8 a = pack_bf16x8(fa);
-                accK = mfma16x16x32(a, bK[kk], accK);
-                accQ = mfma16x16x32(a, bQ[kk], accQ);
             }
-            const int rr = 16 * i + l16;
+            f32x4 ck = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                float bk[8], bq[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bk[e] = static_cast<float>(kk8[kk][e]) * rk * fj[kk][e];
+                    bq[e] = static_cast<float>(kq[kk][e]) * rq * fj[kk][e];
+                }
+                const bf16x8 a = sKh[j][kk][lane];
+                ck = mfma16x16x32(a, pack_bf16x8(bk), ck);
+                cq = mfma16x16x32(a, pack_bf16x8(bq), cq);
+            }
             f32x4 mk, aq;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const int ss = 16 * j + 4 * g4 + ii;
-                mk[ii] = ss < rr ? sBeta[rr] * accK[ii] : 0.0f;
-                aq[ii] = ss <= rr ? accQ[ii] : 0.0f;
+                const int s = 16 * j + 4 * g4 + ii;
+                mk[ii] = s < r ? b_r * ck[ii] : 0.0f;
+                aq[ii] = s <= r ? cq[ii] : 0.0f;
             }
-            *reinterpret_cast<f32x4*>(&sM[rr][16 * j + 4 * g4]) = mk;
-            *reinterpret_cast<bf16x4*>(wA + (int64_t)rr * BTP + 16 * j + 4 * g4) = pack_bf16x4(aq);
+            *reinterpret_cast<f32x4*>(&sM[r][16 * j + 4 * g4]) = mk;
+            *reinterpret_cast<bf16x4*>(wA + swz<BTP>(r, 16 * j + 4 * g4)) = pack_bf16x4(aq);
         }
+        for (int j = wave + 1; j < BTP / 16; ++j)   // above the diagonal (and padding)
+            *reinterpret_cast<bf16x4*>(wA + swz<BTP>(r, 16 * j + 4 * g4)) = bf16x4{};
     }
-    __syncthreads();
+    __syncthreads();                          // sM ready
 
-    // 4a. Diagonal blocks of X = (I + M)^{-1}: forward substitution, one wave
-    //     per block, one lane per column.
-    if (wave < NS && l16 == lane) {
-        const int b0 = 16 * wave;
-        float xcol[16];
+    // 4a. Diagonal blocks of X: forward substitution, lane c of wave w solves
+    //     column c of X_ww.
+    if (tok_wave && lane < 16) {
+        const int b0 = 16 * wave, c = lane;
+        float xc[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            float acc = rr == lane ? 1.0f : 0.0f;
+            float acc = rr == c ? 1.0f : 0.0f;
 #pragma unroll
-            for (int s = 0; s < rr; ++s) acc -= sM[b0 + rr][b0 + s] * xcol[s];
-            xcol[rr] = acc;
-            sX[b0 + rr][b0 + lane] = acc;
+            for (int s = 0; s < rr; ++s) acc -= sM[b0 + rr][b0 + s] * xc[s];
+            xc[rr] = acc;
+            sX[b0 + rr][b0 + c] = acc;
         }
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 4)
+            *reinterpret_cast<float4*>(&sXt[b0 + c][b0 + rr]) = make_float4(xc[rr], xc[rr + 1], xc[rr + 2], xc[rr + 3]);
     }
-    __syncthreads();
-
     // 4b. Off-diagonal blocks, block row by block row:
     //     X_ij = -X_ii sum_{j<=m<i} M_im X_mj  (fp32 MFMA); wave j does (i, j).
+    //     MFMA step kb uses K index 4 (l/16) + kb in lane l, so A and B are
+    //     read as float4 rows of M, X and X^T.
     for (int i = 1; i < NS; ++i) {
+        __syncthreads();
         if (wave < i) {
             const int j = wave;
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
             for (int m = j; m < i; ++m) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&sM[16 * i + l16][16 * m + 4 * g4]);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(&sXt[16 * j + l16][16 * m + 4 * g4]);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    y = mfma16x16x4f32(sM[16 * i + l16][16 * m + 4 * kk + g4],
-                                       sX[16 * m + 4 * kk + g4][16 * j + l16], y);
+                for (int kb = 0; kb < 4; ++kb) y = mfma16x16x4f32(a[kb], b[kb], y);
             }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sTmp[wave][4 * g4 + ii][l16] = y[ii];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&sX[16 * i + l16][16 * i + 4 * g4]);
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                z = mfma16x16x4f32(sX[16 * i + l16][16 * i + 4 * kk + g4],
-                                   sTmp[wave][4 * kk + g4][l16], z);
+            for (int kb = 0; kb < 4; ++kb) z = mfma16x16x4f32(a[kb], y[kb], z);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sX[16 * i + 4 * g4 + ii][16 * j + l16] = -z[ii];
+            for (int ii = 0; ii < 4; ++ii) {
+                z[ii] = -z[ii];
+                sX[16 * i + 4 * g4 + ii][16 * j + l16] = z[ii];
+            }
+            *reinterpret_cast<f32x4*>(&sXt[16 * j + l16][16 * i + 4 * g4]) = z;
         }
-        __syncthreads();
     }
+    __syncthreads();                          // X complete
 
-    // 5. With T = X Diag(beta): W^T = K~^T T^T (so each lane stores 4
-    //    consecutive key channels of one W row) and U = T V (4 consecutive
-    //    tokens of one U^T row), on bf16 MFMA up to the diagonal.
+    // T = X Diag(beta) in bf16, zero above the diagonal blocks and in the padding.
+    for (int idx = tid; idx < BT * (BTP / 8); idx += kThreads) {
+        const int rr = idx / (BTP / 8), s0 = 8 * (idx % (BTP / 8));
+        float t8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s = s0 + e;
+            t8[e] = (s < BT && s / 16 <= rr / 16) ? sX[rr][s] * sBeta[s] : 0.0f;
+        }
+        *reinterpret_cast<bf16x8*>(&sT[rr][s0]) = pack_bf16x8(t8);
+    }
+    __syncthreads();                          // sT ready
+
+    // 5. W^T = K~^T T^T (lane: 4 consecutive channels of one W row) and
+    //    U = T V (lane: 4 consecutive tokens of one U^T row), K up to the diagonal.
     {
         constexpr int NTW = (DKP / 16) * NS, NTU = NS * (D / 16);
-        auto t_row = [&](int r, int s0) {           // T[r][s0 .. s0+7] as bf16
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = s0 + e;
-                f[e] = s < BT ? sX[r][s] * sBeta[s] : 0.0f;
-            }
-            return pack_bf16x8(f);
-        };
-        for (int t = wave; t < NTW + NTU; t += 4) {
+        for (int t = wave; t < NTW + NTU; t += kThreads / kWave) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (t < NTW) {
-                const int mt = t / NS, nt = t % NS;             // key tile, token tile
+                const int mt = t / NS, nt = t % NS;             // channel tile, token tile
                 const int kmax = (16 * nt + 15) / 32;
-                for (int kk = 0; kk <= kmax; ++kk) {
-                    const int s0 = 32 * kk + 8 * g4;
-                    acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sKt[16 * mt + l16][s0]),
-                                       t_row(16 * nt + l16, s0), acc);
-                }
-                *reinterpret_cast<bf16x4*>(wW + (int64_t)(16 * nt + l16) * DKP + 16 * mt + 4 * g4) =
-                    pack_bf16x4(acc);
+                for (int kk = 0; kk <= kmax; ++kk)
+                    acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sKt[16 * mt + l16][32 * kk + 8 * g4]),
+                                       *reinterpret_cast<const bf16x8*>(&sT[16 * nt + l16][32 * kk + 8 * g4]), acc);
+                *reinterpret_cast<bf16x4*>(wW + swz<DKP>(16 * nt + l16, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
             } else {
                 const int tt = t - NTW;
                 const int mt = tt / (D / 16), nt = tt % (D / 16);  // token tile, value tile
                 const int kmax = (16 * mt + 15) / 32;
-                for (int kk = 0; kk <= kmax; ++kk) {
-                    const int s0 = 32 * kk + 8 * g4;
-                    acc = mfma16x16x32(t_row(16 * mt + l16, s0),
-                                       *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][s0]), acc);
-                }
-                *reinterpret_cast<bf16x4*>(wU + (int64_t)(16 * nt + l16) * BTP + 16 * mt + 4 * g4) =
-                    pack_bf16x4(acc);
+                for (int kk = 0; kk <= kmax; ++kk)
+                    acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sT[16 * mt + l16][32 * kk + 8 * g4]),
+                                       *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][32 * kk + 8 * g4]), acc);
+                *reinterpret_cast<bf16x4*>(wU + swz<BTP>(16 * nt + l16, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
             }
         }
         if (BTP > BT)
             for (int idx = tid; idx < D * (BTP - BT) / 4; idx += kThreads) {
                 const int row = idx / ((BTP - BT) / 4), c4 = idx % ((BTP - BT) / 4);
-                *reinterpret_cast<bf16x4*>(wU + (int64_t)row * BTP + BT + 4 * c4) = bf16x4{};
+                *reinterpret_cast<bf16x4*>(wU + swz<BTP>(row, BT + 4 * c4)) = bf16x4{};
             }
     }
 }
@@ -496,49 +553,66 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
 // ---------------------------------------------------------------------------
 // chain_kernel: the state-dependent part, serial over a sequence's chunks.
 //
-// One workgroup per (sequence, head, 16-column d_v tile) with eleven waves in
-// four roles.  Each role runs its own loop over the chunks and every role
-// executes the same two barriers per chunk (B1: D is ready; B2: the next S and
-// the next operand stage are ready):
-//   state waves 0-3    D = U - W S for token tile w; then S <- e^{G_C} S + Kb^T D
-//                      for key tiles w, w+4.  S stays in fp32 accumulators and
-//                      is shared as bf16 S^T through a ping-pong LDS tile.
-//   output waves 4-7   O = scale (Q~ S + Aqk D) for token tile w-4, with their
-//                      Q~ and Aqk rows prefetched into registers 3 chunks ahead.
-//   loader waves 8-9   stream each chunk's W, Kb^T, U tile and e^{G_C} into a
-//                      3-stage LDS ring with asynchronous global->LDS loads.
-//   warmer wave 10     asks for this tile's share of the record WARM chunks
+// One workgroup per (sequence, head, 16-column d_v tile) with thirteen waves
+// in four roles.  Each role runs its own loop over the chunks and every role
+// executes the same two barriers per chunk.  Phase 1 (before B1) reads S;
+// phase 2 (between B1 and B2) reads D and writes the next S:
+//   state waves 0-3    phase 1: D = U - W S for token tile w.
+//                      phase 2: S <- e^{G_C} S + Kb^T D for key tiles w, w+4.
+//                      S stays in fp32 accumulators and is shared as bf16 S^T.
+//   output waves 4-7   phase 1: Q~ S;  phase 2: + Aqk D, scaled and stored,
+//                      for token tile w-4.
+//   loader waves 8-11  stream the record into two LDS rings with
+//                      asynchronous global->LDS loads: ring A (W, Q~, the U
+//                      tile; read in phase 1) with 2 stages and ring B (Kb^T,
+//                      Aqk, e^{G_C}; read in phase 2) with 3 stages.  A stage
+//                      is refilled as soon as the phase that reads it has
+//                      passed its barrier.
+//   warmer wave 12     asks for this tile's share of the record WARM chunks
 //                      ahead, so that the L2 of the XCD (shared by all tiles of
 //                      the pair) holds each record before it is streamed; a CU
 //                      reads its L2 several times faster than it pulls from HBM.
-// State waves issue no global loads, and loads with different latencies sit
-// in different waves, so no wave waits on another's prefetch.
-constexpr int kChainWaves = 11;
+// Compute waves issue no global loads, and each loader wave owns one stream,
+// so no wave waits on another's prefetch (waits count per wave, in order).
+// The record's bf16 tiles are stored with swizzled 16-byte chunks (swz), so
+// the linear copies land in LDS in a layout that 16 lanes reading one chunk
+// column of 16 rows read without bank conflicts.
+constexpr int kChainWaves = 13;
 constexpr int kChainThreads = kChainWaves * kWave;
-constexpr int kStages = 3;
+constexpr int kStagesA = 2;
+constexpr int kStagesB = 3;
 constexpr int kWarm = 4;
 
+constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+constexpr int copy_ops(int bytes) { return (bytes + kWave * 16 - 1) / (kWave * 16); }
+
 template <int D, int BT>
-struct ChainStage {
+struct ChainRings {
     using P = Shape<D, BT>;
+    // ring A stage
     static constexpr int W_OFF = 0;                                   // W    [BT][DKP]
-    static constexpr int KB_OFF = W_OFF + BT * P::DKP * 2;            // Kb^T [DKP][BTP]
-    static constexpr int U_OFF = KB_OFF + P::DKP * P::BTP * 2;        // U^T tile [16][BTP]
-    static constexpr int EG_OFF = U_OFF + 16 * P::BTP * 2;            // e^{G_C} [DKP] fp32
-    static constexpr int BYTES = (EG_OFF + P::DKP * 4 + 1023) / 1024 * 1024;
-    // asynchronous 1-KB copies per stage (64 lanes x 16 B)
-    static constexpr int OPS_W = (BT * P::DKP * 2 + 1023) / 1024;
-    static constexpr int OPS_KB = (P::DKP * P::BTP * 2 + 1023) / 1024;
-    static constexpr int OPS_U = (16 * P::BTP * 2 + 1023) / 1024;
-    static constexpr int OPS_EG = (P::DKP * 4 + 1023) / 1024;
-    static constexpr int OPS = OPS_W + OPS_KB + OPS_U + OPS_EG;
+    static constexpr int Q_OFF = W_OFF + BT * P::DKP * 2;             // Q~   [BT][DKP]
+    static constexpr int U_OFF = Q_OFF + BT * P::DKP * 2;             // U^T tile [16][BTP]
+    static constexpr int A_BYTES = round_up(U_OFF + 16 * P::BTP * 2, 512);
+    // ring B stage
+    static constexpr int KB_OFF = 0;                                  // Kb^T [DKP][BTP]
+    static constexpr int AQ_OFF = KB_OFF + P::DKP * P::BTP * 2;       // Aqk  [BT][BTP]
+    static constexpr int EG_OFF = AQ_OFF + BT * P::BTP * 2;           // e^{G_C} [DKP] fp32
+    static constexpr int B_BYTES = round_up(EG_OFF + P::DKP * 4, 512);
+    // asynchronous copies (1 KB each) per stage and loader wave
+    static constexpr int OPS_L0 = copy_ops(BT * P::DKP * 2) + copy_ops(16 * P::BTP * 2);  // W, U
+    static constexpr int OPS_L1 = copy_ops(BT * P::DKP * 2);                              // Q~
+    static constexpr int OPS_L2 = copy_ops(P::DKP * P::BTP * 2);                          // Kb^T
+    static constexpr int OPS_L3 = copy_ops(BT * P::BTP * 2) + copy_ops(P::DKP * 4);       // Aqk, e^G
+    static_assert(kStagesA * OPS_L0 < 64 && kStagesA * OPS_L1 < 64, "vmcnt range");
+    static_assert(kStagesB * OPS_L2 < 64 && kStagesB * OPS_L3 < 64, "vmcnt range");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy `bytes` (a multiple of 16) from global `src` to LDS `dst` in 1-KB
 // asynchronous pieces; every piece is issued (lanes past the end idle), so the
-// number of memory operations is fixed.
+// number of memory operations is copy_ops(bytes).
 __device__ __forceinline__ void copy_async(uint8_t* dst, const uint8_t* src, int bytes, int lane)
 {
     for (int off = 0; off < bytes; off += kWave * 16) {
@@ -556,14 +630,15 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                   const uint8_t* __restrict__ ws)
 {
     using P = Shape<D, BT>;
-    using SG = ChainStage<D, BT>;
+    using R = ChainRings<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS;
     constexpr int TILES = D / 16;                 // column tiles of one (sequence, head)
     constexpr int NKT_W = (P::NMT_K + 3) / 4;     // key m-tiles per state wave
     constexpr int SP = DKP + 8, DP = BTP + 8;     // bf16 pitches of the exchange tiles
 
-    __shared__ __attribute__((aligned(1024))) uint8_t sStage[kStages][SG::BYTES];
-    __shared__ __attribute__((aligned(16))) bf16 sS[2][16][SP];   // bf16 S^T (ping-pong)
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[kStagesA][R::A_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStagesB][R::B_BYTES];
+    __shared__ __attribute__((aligned(16))) bf16 sS[16][SP];      // bf16 S^T of the tile
     __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // bf16 D^T
     __shared__ __attribute__((aligned(1024))) uint8_t sWarm[kWave * 16];   // discarded
 
@@ -614,31 +689,35 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 bf16x4 s4;
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) s4[ii] = static_cast<bf16>(S[j][ii]);
-                *reinterpret_cast<bf16x4*>(&sS[0][l16][16 * kt + 4 * g4]) = s4;
+                *reinterpret_cast<bf16x4*>(&sS[l16][16 * kt + 4 * g4]) = s4;
             }
         }
         if (BTP > BT && wave == 0)                 // token padding of D^T stays zero
             *reinterpret_cast<bf16x4*>(&sD[l16][BT + 4 * g4]) = bf16x4{};
-        lds_barrier();                             // B0: S_0 published, stage 0 loaded
+        lds_barrier();                             // B0: S_0 published
 
         for (int lc = 0; lc < nch; ++lc) {
-            const uint8_t* stg = sStage[lc % kStages];
-            const bf16* sW = reinterpret_cast<const bf16*>(stg + SG::W_OFF);
-            const bf16* sKb = reinterpret_cast<const bf16*>(stg + SG::KB_OFF);
-            const bf16* sU = reinterpret_cast<const bf16*>(stg + SG::U_OFF);
-            const float* sEg = reinterpret_cast<const float*>(stg + SG::EG_OFF);
-            const int cur = lc & 1;
+            const uint8_t* stA = sA[lc % kStagesA];
+            const uint8_t* stB = sB[lc % kStagesB];
+            const bf16* sW = reinterpret_cast<const bf16*>(stA + R::W_OFF);
+            const bf16* sU = reinterpret_cast<const bf16*>(stA + R::U_OFF);
+            const bf16* sKb = reinterpret_cast<const bf16*>(stB + R::KB_OFF);
+            const float* sEg = reinterpret_cast<const float*>(stB + R::EG_OFF);
             if (wave < NS) {                       // D = U - W S, token tile `wave`
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+                const int r = 16 * wave + l16;
 #pragma unroll
-                for (int kk = 0; kk < P::NKK_K; ++kk)
-                    acc = mfma16x16x32(
-                        *reinterpret_cast<const bf16x8*>(sW + (16 * wave + l16) * DKP + 32 * kk + 8 * g4),
-                        *reinterpret_cast<const bf16x8*>(&sS[cur][l16][32 * kk + 8 * g4]), acc);
-                const bf16x4 u4 = *reinterpret_cast<const bf16x4*>(sU + l16 * BTP + 16 * wave + 4 * g4);
+                for (int kk = 0; kk < P::NKK_K; ++kk) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sW + swz<DKP>(r, 32 * kk + 8 * g4));
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
+                    if (kk & 1) acc1 = mfma16x16x32(a, b, acc1);
+                    else acc0 = mfma16x16x32(a, b, acc0);
+                }
+                const bf16x4 u4 = *reinterpret_cast<const bf16x4*>(sU + swz<BTP>(l16, 16 * wave + 4 * g4));
                 bf16x4 d4;
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) d4[ii] = static_cast<bf16>(static_cast<float>(u4[ii]) - acc[ii]);
+                for (int ii = 0; ii < 4; ++ii)
+                    d4[ii] = static_cast<bf16>(static_cast<float>(u4[ii]) - (acc0[ii] + acc1[ii]));
                 *reinterpret_cast<bf16x4*>(&sD[l16][16 * wave + 4 * g4]) = d4;
             }
             lds_barrier();                         // B1
@@ -653,14 +732,14 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_T; ++kk)
                     acc = mfma16x16x32(
-                        *reinterpret_cast<const bf16x8*>(sKb + (16 * kt + l16) * BTP + 32 * kk + 8 * g4),
+                        *reinterpret_cast<const bf16x8*>(sKb + swz<BTP>(16 * kt + l16, 32 * kk + 8 * g4)),
                         *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc);
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) S[j][ii] = acc[ii];
                 bf16x4 s4;
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) s4[ii] = static_cast<bf16>(S[j][ii]);
-                *reinterpret_cast<bf16x4*>(&sS[cur ^ 1][l16][16 * kt + 4 * g4]) = s4;
+                *reinterpret_cast<bf16x4*>(&sS[l16][16 * kt + 4 * g4]) = s4;
             }
             const int pos = (lc + 1) * BT;         // checkpoint at this chunk's end
             if (ckpt && interval > 0 && pos <= len && pos % interval == 0) {
@@ -693,89 +772,96 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
         // ---------------- output waves ----------------
         const int tt = wave - 4;                   // token tile
         const bool active = tt < NS;
-        const int kmax = (16 * tt + 15) / 32;
-        struct OutOps { bf16x8 q[P::NKK_K]; bf16x8 a[P::NKK_T]; };
-        auto load_ops = [&](OutOps& o, int lc) {
-            const uint8_t* rec = record(lc);
-            const bf16* wQ = reinterpret_cast<const bf16*>(rec) + P::OFF_Q;
-            const bf16* wA = reinterpret_cast<const bf16*>(rec) + P::OFF_A;
-            const int64_t row = 16 * (active ? tt : 0) + l16;
-#pragma unroll
-            for (int kk = 0; kk < P::NKK_K; ++kk)
-                o.q[kk] = *reinterpret_cast<const bf16x8*>(wQ + row * DKP + 32 * kk + 8 * g4);
-#pragma unroll
-            for (int kk = 0; kk < P::NKK_T; ++kk)
-                o.a[kk] = *reinterpret_cast<const bf16x8*>(wA + row * BTP + 32 * kk + 8 * g4);
-        };
-        auto step = [&](const OutOps& o, int lc) {
-            const int cur = lc & 1;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int kmax = (16 * tt + 15) / 32;      // Aqk is zero beyond the diagonal
+        const int r = 16 * (active ? tt : 0) + l16;
+        lds_barrier();                             // B0
+        for (int lc = 0; lc < nch; ++lc) {
+            const bf16* sQ = reinterpret_cast<const bf16*>(sA[lc % kStagesA] + R::Q_OFF);
+            const bf16* sAq = reinterpret_cast<const bf16*>(sB[lc % kStagesB] + R::AQ_OFF);
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
             if (active) {
 #pragma unroll
-                for (int kk = 0; kk < P::NKK_K; ++kk)
-                    acc = mfma16x16x32(o.q[kk], *reinterpret_cast<const bf16x8*>(&sS[cur][l16][32 * kk + 8 * g4]), acc);
+                for (int kk = 0; kk < P::NKK_K; ++kk) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + swz<DKP>(r, 32 * kk + 8 * g4));
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
+                    if (kk & 1) acc1 = mfma16x16x32(a, b, acc1);
+                    else acc0 = mfma16x16x32(a, b, acc0);
+                }
             }
             lds_barrier();                         // B1
             if (active) {
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_T; ++kk)
                     if (kk <= kmax)
-                        acc = mfma16x16x32(o.a[kk], *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc);
+                        acc0 = mfma16x16x32(
+                            *reinterpret_cast<const bf16x8*>(sAq + swz<BTP>(r, 32 * kk + 8 * g4)),
+                            *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc0);
                 const int64_t tc = s_begin + (int64_t)lc * BT;
                 const int clen = min(BT, len - lc * BT);
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    const int r = 16 * tt + 4 * g4 + ii;
-                    if (r < clen) out[(tc + r) * os + (int64_t)h * D + col] = from_f32<AT>(scale * acc[ii]);
+                    const int rr = 16 * tt + 4 * g4 + ii;
+                    if (rr < clen)
+                        out[(tc + rr) * os + (int64_t)h * D + col] = from_f32<AT>(scale * (acc0[ii] + acc1[ii]));
                 }
             }
-        };
-        OutOps o0, o1, o2;
-        load_ops(o0, 0);
-        load_ops(o1, 1);
-        lds_barrier();                             // B0
-        for (int lc = 0; lc < nch; lc += 3) {
-            load_ops(o2, lc + 2);
-            step(o0, lc);
             lds_barrier();                         // B2
-            if (lc + 1 >= nch) break;
-            load_ops(o0, lc + 3);
-            step(o1, lc + 1);
-            lds_barrier();
-            if (lc + 2 >= nch) break;
-            load_ops(o1, lc + 4);
-            step(o2, lc + 2);
-            lds_barrier();
         }
     } else if (wave < 10) {
-        // ---------------- loader waves ----------------
-        // Stage copies are split between the two loader waves; each wave waits
-        // only for its own copies (vmcnt counts per wave, in issue order).
+        // ---------------- ring A loaders ----------------
+        // Stage lc % 2 is read in phase 1 of chunk lc; after B1 of chunk lc it
+        // is refilled with chunk lc + 2, which must be complete by B2 of
+        // chunk lc + 1.
         const int lw = wave - 8;
-        auto issue_stage = [&](int lc) {
-            uint8_t* dst = sStage[lc % kStages];
+        auto issue = [&](int lc) {
+            uint8_t* dst = sA[lc % kStagesA];
             const uint8_t* rec = record(lc);
             if (lw == 0) {
-                copy_async(dst + SG::W_OFF, rec + P::OFF_W * 2, BT * DKP * 2, lane);
-                copy_async(dst + SG::U_OFF, rec + (P::OFF_U + (int64_t)n0 * BTP) * 2, 16 * BTP * 2, lane);
+                copy_async(dst + R::W_OFF, rec + P::OFF_W * 2, BT * DKP * 2, lane);
+                copy_async(dst + R::U_OFF, rec + (P::OFF_U + (int64_t)n0 * BTP) * 2, 16 * BTP * 2, lane);
             } else {
-                copy_async(dst + SG::KB_OFF, rec + P::OFF_KB * 2, DKP * BTP * 2, lane);
-                copy_async(dst + SG::EG_OFF, rec + P::EG_BYTE_OFF, DKP * 4, lane);
+                copy_async(dst + R::Q_OFF, rec + P::OFF_Q * 2, BT * DKP * 2, lane);
             }
         };
-        // Copies one loader wave issues per stage (the larger of the two halves).
-        issue_stage(0);
-        issue_stage(1);
-        // wait for stage 0: at most one stage's copies outstanding
-        if (lw == 0) wait_vmcnt<SG::OPS_W + SG::OPS_U>();
-        else wait_vmcnt<SG::OPS_KB + SG::OPS_EG>();
+        issue(0);
+        issue(1);
+        if (lw == 0) wait_vmcnt<R::OPS_L0>();      // chunk 0 complete
+        else wait_vmcnt<R::OPS_L1>();
         lds_barrier();                             // B0
         for (int lc = 0; lc < nch; ++lc) {
             lds_barrier();                         // B1
-            issue_stage(lc + 2);                   // into the stage chunk lc-1 used
-            if (lw == 0) wait_vmcnt<SG::OPS_W + SG::OPS_U>();   // stage lc+1 complete
-            else wait_vmcnt<SG::OPS_KB + SG::OPS_EG>();
+            issue(lc + 2);
+            if (lw == 0) wait_vmcnt<R::OPS_L0>();  // chunk lc + 1 complete
+            else wait_vmcnt<R::OPS_L1>();
             lds_barrier();                         // B2
+        }
+        wait_vmcnt<0>();
+    } else if (wave < 12) {
+        // ---------------- ring B loaders ----------------
+        // Stage lc % 3 is read in phase 2 of chunk lc; after B2 of chunk lc it
+        // is refilled with chunk lc + 3.  Chunk lc must be complete by B1 of
+        // chunk lc, with chunks lc + 1 and lc + 2 still in flight.
+        const int lw = wave - 10;
+        auto issue = [&](int lc) {
+            uint8_t* dst = sB[lc % kStagesB];
+            const uint8_t* rec = record(lc);
+            if (lw == 0) {
+                copy_async(dst + R::KB_OFF, rec + P::OFF_KB * 2, DKP * BTP * 2, lane);
+            } else {
+                copy_async(dst + R::AQ_OFF, rec + P::OFF_A * 2, BT * BTP * 2, lane);
+                copy_async(dst + R::EG_OFF, rec + P::EG_BYTE_OFF, DKP * 4, lane);
+            }
+        };
+        issue(0);
+        issue(1);
+        issue(2);
+        lds_barrier();                             // B0
+        for (int lc = 0; lc < nch; ++lc) {
+            if (lw == 0) wait_vmcnt<2 * R::OPS_L2>();
+            else wait_vmcnt<2 * R::OPS_L3>();
+            lds_barrier();                         // B1
+            lds_barrier();                         // B2
+            issue(lc + 3);
         }
         wait_vmcnt<0>();
     } else {
