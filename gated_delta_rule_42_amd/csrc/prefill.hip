@@ -46,6 +46,10 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;   // four waves per workgroup
+// Largest total log-decay of one chunk (per channel) for which the Gram
+// products use the chunk start as the only reference point: e^{80} and
+// e^{-80} are far inside the fp32 / bf16 range.
+constexpr float kMaxLogDecay = 80.0f;
 
 template <int D, int BT>
 struct Shape {
@@ -235,7 +239,7 @@ __device__ __forceinline__ bf16x8 identity_half(int half, int lane)
 //      been transposed with identity MFMA products in step 2.
 // Record stores are 8- or 16-byte vector stores in the swizzled layout.
 template <int D, int BT, typename AT>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kThreads, 2)
 void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* __restrict__ v,
                   int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ g,
                   const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
@@ -247,15 +251,30 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     constexpr int XP = BT + 4;               // fp32 pitch of the X / M tiles
     constexpr int TP = BTP + 8;              // bf16 pitch of the token-contiguous tiles
 
+    // LDS regions are reused once the phase that reads them has passed a
+    // barrier, so that two workgroups fit on one CU:
+    //   R1: K^ fragments (Gram)  ->  X^T (solve)  ->  K~^T (W)
+    //   R2: M (solve)                             ->  V^T (U)
+    constexpr int KH_BYTES = NS * NKK * kWave * 16;
+    constexpr int XT_BYTES = BT * XP * 4;
+    constexpr int KT_BYTES = DKP * TP * 2;
+    constexpr int R1_BYTES = KH_BYTES > XT_BYTES ? (KH_BYTES > KT_BYTES ? KH_BYTES : KT_BYTES)
+                                                 : (XT_BYTES > KT_BYTES ? XT_BYTES : KT_BYTES);
+    constexpr int R2_BYTES = XT_BYTES > KT_BYTES ? XT_BYTES : KT_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t sR1[R1_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sR2[R2_BYTES];
+    auto sKh = reinterpret_cast<bf16x8 (*)[NKK][kWave]>(sR1);            // [NS][NKK][64]
+    auto sXt = reinterpret_cast<float (*)[XP]>(sR1);                     // X^T [BT][XP]
+    auto sKt = reinterpret_cast<bf16 (*)[TP]>(sR1);                      // K~^T [DKP][TP]
+    auto sM = reinterpret_cast<float (*)[XP]>(sR2);                      // M [BT][XP]
+    auto sVt = reinterpret_cast<bf16 (*)[TP]>(sR2);                      // V^T [DKP][TP]
+    __shared__ __attribute__((aligned(16))) float sXd[NS][16][20];       // diagonal blocks of X
+    __shared__ __attribute__((aligned(16))) bf16 sT[BT][TP];             // T = X Diag(beta)
     __shared__ __attribute__((aligned(16))) float sTot[4][DKP];          // tile totals of g
     __shared__ __attribute__((aligned(16))) float sE[4][DKP];            // e^{tile total}
-    __shared__ __attribute__((aligned(16))) bf16x8 sKh[NS][NKK][kWave];  // K^ fragments
-    __shared__ __attribute__((aligned(16))) float sM[BT][XP];            // strict_lower(Diag(beta) K~ K^T)
-    __shared__ __attribute__((aligned(16))) float sX[BT][XP];            // X
-    __shared__ __attribute__((aligned(16))) float sXt[BT][XP];           // X^T
-    __shared__ __attribute__((aligned(16))) bf16 sT[BT][TP];             // T = X Diag(beta)
-    __shared__ __attribute__((aligned(16))) bf16 sKt[DKP][TP];           // K~^T
-    __shared__ __attribute__((aligned(16))) bf16 sVt[DKP][TP];           // V^T
+    __shared__ __attribute__((aligned(16))) float sBef[4][DKP];          // e^{G_b}
+    __shared__ __attribute__((aligned(16))) float sAft[4][DKP];          // e^{G_C - G_b}
+    __shared__ __attribute__((aligned(16))) float sInv[4][DKP];          // e^{-G_b}
     __shared__ __attribute__((aligned(16))) float sBeta[BTP];
 
     const int x = blockIdx.x, h = blockIdx.y;
@@ -336,114 +355,125 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     }
     __syncthreads();
 
-    // Tile exponentials and the chunk's total decay.
-    for (int idx = tid; idx < NS * DKP; idx += kThreads)
-        sE[idx / DKP][idx % DKP] = __expf(sTot[idx / DKP][idx % DKP]);
+    // Per-tile reference points and the chunk's total decay, per channel c:
+    //   sBef[w][c] = e^{G_{b_w}},  sAft[w][c] = e^{G_C - G_{b_w}},
+    //   sInv[w][c] = e^{-G_{b_w}},  sE[w][c] = e^{tile total w},  e^{G_C} -> record.
+    // A chunk whose total decay stays above e^{-kMaxLogDecay} on every channel
+    // takes the single-reference path: e^{G} and e^{-G} are then both
+    // representable and one factor pair serves every Gram block.
+    bool strong = false;
     for (int c = tid; c < DKP; c += kThreads) {
         float tot = 0.0f;
         for (int j = 0; j < NS; ++j) tot += sTot[j][c];
+        float pre = 0.0f;
+        for (int j = 0; j < NS; ++j) {
+            const float tj = sTot[j][c];
+            sBef[j][c] = __expf(pre);
+            sInv[j][c] = __expf(-pre);
+            sAft[j][c] = __expf(tot - pre);
+            sE[j][c] = __expf(tj);
+            pre += tj;
+        }
         wEg[c] = c < D ? __expf(tot) : 0.0f;
+        strong |= tot < -kMaxLogDecay;
     }
-    // The scan is relative to the tile's reference point: gv = G_r - G_{b_w}.
-    float fw[NKK][8];                         // e^{G_r - G_{b_w}}
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fw[kk][e] = __expf(gv[kk][e]);
-    __syncthreads();                          // sE ready
+    strong = __syncthreads_or(strong) != 0;
 
-    // 2. Factors.  For this tile (reference b_w):
-    //    K^ = k / f_w -> LDS (Gram A side); Kb = K^ * prod_{m>=w} E_m -> record;
-    //    f_0 = f_w * prod_{m<w} E_m: Q~ = q f_0 -> record, K~ = k f_0 -> LDS (transposed).
+    // 2. Factors, with f_w = e^{G_r - G_{b_w}} (the scan is tile-relative):
+    //    K^ = k / f_w (tile reference; times e^{-G_{b_w}} for the chunk-start
+    //    reference of the single-reference path) -> LDS;
+    //    Kb = k e^{G_C - G_r} -> record (transposed);
+    //    Q~ = q e^{G_r} -> record;  K~ = k e^{G_r} -> LDS (transposed).
+    bf16x8 qt0[NKK], kt0[NKK];
     if (tok_wave) {
         const bf16x8 id0 = identity_half(0, lane), id1 = identity_half(1, lane);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int c0 = 32 * kk + 8 * g4;
-            float before[8], after[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { before[e] = 1.0f; after[e] = 1.0f; }
-            for (int m = 0; m < NS; ++m) {
-                const float4 a = *reinterpret_cast<const float4*>(&sE[m][c0]);
-                const float4 b = *reinterpret_cast<const float4*>(&sE[m][c0 + 4]);
-                const float em[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (m < wave) before[e] *= em[e];
-                    else after[e] *= em[e];
-                }
-            }
+            const float4 bf0 = *reinterpret_cast<const float4*>(&sBef[wave][c0]);
+            const float4 bf1 = *reinterpret_cast<const float4*>(&sBef[wave][c0 + 4]);
+            const float4 af0 = *reinterpret_cast<const float4*>(&sAft[wave][c0]);
+            const float4 af1 = *reinterpret_cast<const float4*>(&sAft[wave][c0 + 4]);
+            const float4 iv0 = *reinterpret_cast<const float4*>(&sInv[wave][c0]);
+            const float4 iv1 = *reinterpret_cast<const float4*>(&sInv[wave][c0 + 4]);
+            const float bef[8] = {bf0.x, bf0.y, bf0.z, bf0.w, bf1.x, bf1.y, bf1.z, bf1.w};
+            const float aft[8] = {af0.x, af0.y, af0.z, af0.w, af1.x, af1.y, af1.z, af1.w};
+            const float inb[8] = {iv0.x, iv0.y, iv0.z, iv0.w, iv1.x, iv1.y, iv1.z, iv1.w};
             float kh[8], kb[8], qt[8], kt[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                const float fw = __expf(gv[kk][e]);
+                const float inv = __builtin_amdgcn_rcpf(fw);
+                const float f0 = fw * bef[e];
                 const float kn = static_cast<float>(kk8[kk][e]) * rk;
-                const float inv = __builtin_amdgcn_rcpf(fw[kk][e]);
-                const float f0 = fw[kk][e] * before[e];
-                kh[e] = kn * inv;
-                kb[e] = kh[e] * after[e];
+                const float khw = kn * inv;
+                kh[e] = strong ? khw : khw * inb[e];
+                kb[e] = khw * aft[e];
                 qt[e] = static_cast<float>(kq[kk][e]) * rq * f0;
                 kt[e] = kn * f0;
+                gv[kk][e] = fw;                 // keep f_w for the multi-reference path
             }
             sKh[wave][kk][lane] = pack_bf16x8(kh);
-            *reinterpret_cast<bf16x8*>(wQ + swz<DKP>(r, c0)) = pack_bf16x8(qt);
-            // Transposes through the identity products: lane l gets channel
+            qt0[kk] = pack_bf16x8(qt);
+            kt0[kk] = pack_bf16x8(kt);
+            *reinterpret_cast<bf16x8*>(wQ + swz<DKP>(r, c0)) = qt0[kk];
+            // Kb^T through the identity products: lane l gets channel
             // 32 kk + 16 half + l % 16, tokens 16 w + 4 (l / 16) .. + 3.
-            const bf16x8 akb = pack_bf16x8(kb), akt = pack_bf16x8(kt);
+            const bf16x8 akb = pack_bf16x8(kb);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int c = 32 * kk + 16 * half + l16;
-                const bf16x8 id = half ? id1 : id0;
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 tb = mfma16x16x32(akb, id, zero);
-                const f32x4 tk = mfma16x16x32(akt, id, zero);
-                const f32x4 tv = mfma16x16x32(kv[kk], id, zero);
-                *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(c, 16 * wave + 4 * g4)) = pack_bf16x4(tb);
-                *reinterpret_cast<bf16x4*>(&sKt[c][16 * wave + 4 * g4]) = pack_bf16x4(tk);
-                *reinterpret_cast<bf16x4*>(&sVt[c][16 * wave + 4 * g4]) = pack_bf16x4(tv);
+                const f32x4 tb = mfma16x16x32(akb, half ? id1 : id0, zero);
+                *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(32 * kk + 16 * half + l16, 16 * wave + 4 * g4)) =
+                    pack_bf16x4(tb);
             }
         }
     }
-    if (BTP > BT) {                           // token padding of the transposed tiles
+    if (BTP > BT) {                           // token padding of Kb^T
         for (int idx = tid; idx < DKP * (BTP - BT) / 4; idx += kThreads) {
             const int c = idx / ((BTP - BT) / 4), s = BT + 4 * (idx % ((BTP - BT) / 4));
-            *reinterpret_cast<bf16x4*>(&sKt[c][s]) = bf16x4{};
-            *reinterpret_cast<bf16x4*>(&sVt[c][s]) = bf16x4{};
             *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(c, s)) = bf16x4{};
         }
     }
-    __syncthreads();                          // sKh, sKt, sVt ready
+    __syncthreads();                          // sKh ready
 
-    // 3. Gram blocks (w, j), j <= w:  C[s][r] = K^_s . (f_j k_r)  and  K^_s . (f_j q_r).
+    // 3. Gram blocks (w, j), j <= w, computed transposed: C[s][r], lane l
+    //    holding row r = 16 w + l % 16 and columns s = 16 j + 4 (l / 16) .. + 3.
+    //    Single reference: C = K^_s . K~_r with K^ = k e^{-G}, K~ = k e^{G}.
+    //    Multi-reference (strong decay): the reference of block (w, j) is
+    //    b_j; the row side is k_r f_j with f_j = f_{j+1} e^{tile total j} <= 1,
+    //    the column side K^_s = k_s e^{G_{b_j} - G_s} written by wave j.
     if (tok_wave) {
-        float fj[NKK][8];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) fj[kk][e] = fw[kk][e];
         for (int j = wave; j >= 0; --j) {
-            if (j < wave) {                   // f_j = f_{j+1} * E_j
+            f32x4 ck = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
+            if (!strong) {
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const bf16x8 a = sKh[j][kk][lane];
+                    ck = mfma16x16x32(a, kt0[kk], ck);
+                    cq = mfma16x16x32(a, qt0[kk], cq);
+                }
+            } else {
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
                     const int c0 = 32 * kk + 8 * g4;
-                    const float4 a = *reinterpret_cast<const float4*>(&sE[j][c0]);
-                    const float4 b = *reinterpret_cast<const float4*>(&sE[j][c0 + 4]);
-                    const float em[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                    if (j < wave) {             // gv holds f_{j+1}; advance to f_j
+                        const float4 a = *reinterpret_cast<const float4*>(&sE[j][c0]);
+                        const float4 b = *reinterpret_cast<const float4*>(&sE[j][c0 + 4]);
+                        const float em[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) fj[kk][e] *= em[e];
+                        for (int e = 0; e < 8; ++e) gv[kk][e] *= em[e];
+                    }
+                    float bk[8], bq[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        bk[e] = static_cast<float>(kk8[kk][e]) * rk * gv[kk][e];
+                        bq[e] = static_cast<float>(kq[kk][e]) * rq * gv[kk][e];
+                    }
+                    const bf16x8 a = sKh[j][kk][lane];
+                    ck = mfma16x16x32(a, pack_bf16x8(bk), ck);
+                    cq = mfma16x16x32(a, pack_bf16x8(bq), cq);
                 }
-            }
-            f32x4 ck = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                float bk[8], bq[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bk[e] = static_cast<float>(kk8[kk][e]) * rk * fj[kk][e];
-                    bq[e] = static_cast<float>(kq[kk][e]) * rq * fj[kk][e];
-                }
-                const bf16x8 a = sKh[j][kk][lane];
-                ck = mfma16x16x32(a, pack_bf16x8(bk), ck);
-                cq = mfma16x16x32(a, pack_bf16x8(bq), cq);
             }
             f32x4 mk, aq;
 #pragma unroll
@@ -457,11 +487,14 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
         }
         for (int j = wave + 1; j < BTP / 16; ++j)   // above the diagonal (and padding)
             *reinterpret_cast<bf16x4*>(wA + swz<BTP>(r, 16 * j + 4 * g4)) = bf16x4{};
+        // T is zero above the diagonal blocks (and in the token padding).
+        for (int cc = 16 * (wave + 1) + 4 * g4; cc < BTP; cc += 16)
+            *reinterpret_cast<bf16x4*>(&sT[r][cc]) = bf16x4{};
     }
     __syncthreads();                          // sM ready
 
-    // 4a. Diagonal blocks of X: forward substitution, lane c of wave w solves
-    //     column c of X_ww.
+    // 4a. Diagonal blocks of X = (I + M)^{-1}: forward substitution, lane c
+    //     of wave w solves column c of X_ww; T = X Diag(beta) alongside.
     if (tok_wave && lane < 16) {
         const int b0 = 16 * wave, c = lane;
         float xc[16];
@@ -471,7 +504,8 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
 #pragma unroll
             for (int s = 0; s < rr; ++s) acc -= sM[b0 + rr][b0 + s] * xc[s];
             xc[rr] = acc;
-            sX[b0 + rr][b0 + c] = acc;
+            sXd[wave][rr][c] = acc;
+            sT[b0 + rr][b0 + c] = static_cast<bf16>(acc * b_r);   // b_r: beta of token b0 + c
         }
 #pragma unroll
         for (int rr = 0; rr < 16; rr += 4)
@@ -492,62 +526,82 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) y = mfma16x16x4f32(a[kb], b[kb], y);
             }
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&sX[16 * i + l16][16 * i + 4 * g4]);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&sXd[i][l16][4 * g4]);
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) z = mfma16x16x4f32(a[kb], y[kb], z);
+            const float bs = sBeta[16 * j + l16];
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 z[ii] = -z[ii];
-                sX[16 * i + 4 * g4 + ii][16 * j + l16] = z[ii];
+                sT[16 * i + 4 * g4 + ii][16 * j + l16] = static_cast<bf16>(z[ii] * bs);
             }
             *reinterpret_cast<f32x4*>(&sXt[16 * j + l16][16 * i + 4 * g4]) = z;
         }
     }
-    __syncthreads();                          // X complete
+    __syncthreads();                          // X and T complete; M and X^T dead
 
-    // T = X Diag(beta) in bf16, zero above the diagonal blocks and in the padding.
-    for (int idx = tid; idx < BT * (BTP / 8); idx += kThreads) {
-        const int rr = idx / (BTP / 8), s0 = 8 * (idx % (BTP / 8));
-        float t8[8];
+    // K~^T and V^T through the identity products (into the regions of X^T and M).
+    if (tok_wave) {
+        const bf16x8 id0 = identity_half(0, lane), id1 = identity_half(1, lane);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s = s0 + e;
-            t8[e] = (s < BT && s / 16 <= rr / 16) ? sX[rr][s] * sBeta[s] : 0.0f;
-        }
-        *reinterpret_cast<bf16x8*>(&sT[rr][s0]) = pack_bf16x8(t8);
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const bf16x8 id = half ? id1 : id0;
+                const f32x4 tk = mfma16x16x32(kt0[kk], id, zero);
+                const f32x4 tv = mfma16x16x32(kv[kk], id, zero);
+                const int c = 32 * kk + 16 * half + l16;
+                *reinterpret_cast<bf16x4*>(&sKt[c][16 * wave + 4 * g4]) = pack_bf16x4(tk);
+                *reinterpret_cast<bf16x4*>(&sVt[c][16 * wave + 4 * g4]) = pack_bf16x4(tv);
+            }
     }
-    __syncthreads();                          // sT ready
+    if (BTP > BT) {                           // token padding of the transposed tiles
+        for (int idx = tid; idx < DKP * (BTP - BT) / 4; idx += kThreads) {
+            const int c = idx / ((BTP - BT) / 4), s = BT + 4 * (idx % ((BTP - BT) / 4));
+            *reinterpret_cast<bf16x4*>(&sKt[c][s]) = bf16x4{};
+            *reinterpret_cast<bf16x4*>(&sVt[c][s]) = bf16x4{};
+        }
+    }
+    __syncthreads();                          // K~^T, V^T ready
 
-    // 5. W^T = K~^T T^T (lane: 4 consecutive channels of one W row) and
-    //    U = T V (lane: 4 consecutive tokens of one U^T row), K up to the diagonal.
-    {
-        constexpr int NTW = (DKP / 16) * NS, NTU = NS * (D / 16);
-        for (int t = wave; t < NTW + NTU; t += kThreads / kWave) {
+    // 5. Wave w: the rows of token tile w.  W^T = K~^T T^T (lane: 4
+    //    consecutive channels of one W row) and U = T V (lane: 4 consecutive
+    //    tokens of one U^T row); the T fragment is the same for every tile and
+    //    K stops at the diagonal block.
+    if (tok_wave) {
+        const int kmax = (16 * wave + 15) / 32;
+        bf16x8 tf[P::NKK_T];
+#pragma unroll
+        for (int kk = 0; kk < P::NKK_T; ++kk)
+            tf[kk] = kk <= kmax ? *reinterpret_cast<const bf16x8*>(&sT[r][32 * kk + 8 * g4]) : bf16x8{};
+#pragma unroll
+        for (int mt = 0; mt < DKP / 16; ++mt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (t < NTW) {
-                const int mt = t / NS, nt = t % NS;             // channel tile, token tile
-                const int kmax = (16 * nt + 15) / 32;
-                for (int kk = 0; kk <= kmax; ++kk)
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_T; ++kk)
+                if (kk <= kmax)
                     acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sKt[16 * mt + l16][32 * kk + 8 * g4]),
-                                       *reinterpret_cast<const bf16x8*>(&sT[16 * nt + l16][32 * kk + 8 * g4]), acc);
-                *reinterpret_cast<bf16x4*>(wW + swz<DKP>(16 * nt + l16, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
-            } else {
-                const int tt = t - NTW;
-                const int mt = tt / (D / 16), nt = tt % (D / 16);  // token tile, value tile
-                const int kmax = (16 * mt + 15) / 32;
-                for (int kk = 0; kk <= kmax; ++kk)
-                    acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sT[16 * mt + l16][32 * kk + 8 * g4]),
-                                       *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][32 * kk + 8 * g4]), acc);
-                *reinterpret_cast<bf16x4*>(wU + swz<BTP>(16 * nt + l16, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
-            }
+                                       tf[kk], acc);
+            *reinterpret_cast<bf16x4*>(wW + swz<DKP>(r, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
         }
-        if (BTP > BT)
-            for (int idx = tid; idx < D * (BTP - BT) / 4; idx += kThreads) {
-                const int row = idx / ((BTP - BT) / 4), c4 = idx % ((BTP - BT) / 4);
-                *reinterpret_cast<bf16x4*>(wU + swz<BTP>(row, BT + 4 * c4)) = bf16x4{};
-            }
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_T; ++kk)
+                if (kk <= kmax)
+                    acc = mfma16x16x32(tf[kk],
+                                       *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][32 * kk + 8 * g4]), acc);
+            *reinterpret_cast<bf16x4*>(wU + swz<BTP>(16 * nt + l16, 16 * wave + 4 * g4)) = pack_bf16x4(acc);
+        }
     }
+    if (BTP > BT)
+        for (int idx = tid; idx < D * (BTP - BT) / 4; idx += kThreads) {
+            const int row = idx / ((BTP - BT) / 4), c4 = idx % ((BTP - BT) / 4);
+            *reinterpret_cast<bf16x4*>(wU + swz<BTP>(row, BT + 4 * c4)) = bf16x4{};
+        }
 }
 
 // ---------------------------------------------------------------------------

@@ -94,14 +94,14 @@ class DecodeCase:
     l2norm_qk: bool = False
 
 
-def _draw_tokens(rng, T, H, dk, dv, act_dtype, qk_unit=True):
+def _draw_tokens(rng, T, H, dk, dv, act_dtype, qk_unit=True, g_scale=1.0):
     q = rng.standard_normal((T, H, dk))
     k = rng.standard_normal((T, H, dk))
     if qk_unit:
         q, k = _unit_rows(q), _unit_rows(k)
     v = rng.standard_normal((T, H, dv))
     beta = _sigmoid(rng.standard_normal((T, H)))
-    g = _neg_softplus(rng.standard_normal((T, H, dk)))
+    g = g_scale * _neg_softplus(rng.standard_normal((T, H, dk)))
     return (_to(q, act_dtype), _to(k, act_dtype), _to(v, act_dtype),
             _to(g, F32), _to(beta, F32))
 
@@ -118,7 +118,7 @@ def random_prefill(seed: int, lengths, H: int, dk: int, dv: int, *,
                    act_dtype=BF16, state_dtype=F32, n_slots: int | None = None,
                    slots=None, has_init=None, chunk_size: int = 64,
                    ckpt_interval: int = 0, scale: float = 1.0, state_std: float = 0.02,
-                   qk_unit: bool = True, l2norm_qk: bool = False,
+                   qk_unit: bool = True, l2norm_qk: bool = False, g_scale: float = 1.0,
                    name: str = "random_prefill") -> PrefillCase:
     """A varlen prefill with explicit structure.  `slots` defaults to distinct
     random slots; `has_init` None means every sequence carries a state."""
@@ -133,7 +133,7 @@ def random_prefill(seed: int, lengths, H: int, dk: int, dv: int, *,
     cu = np.zeros(N + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     T = int(cu[-1])
-    q, k, v, g, beta = _draw_tokens(rng, T, H, dk, dv, act_dtype, qk_unit)
+    q, k, v, g, beta = _draw_tokens(rng, T, H, dk, dv, act_dtype, qk_unit, g_scale)
     pool = _draw_pool(rng, n_slots, H, dk, dv, state_dtype, state_std)
     hi = None if has_init is None else torch.tensor(np.asarray(has_init, dtype=np.uint8))
     return PrefillCase(name, q, k, v, g, beta, torch.from_numpy(cu), pool,

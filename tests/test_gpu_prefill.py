@@ -49,6 +49,15 @@ def test_prefill_l2norm_flag():
     check_prefill(case, gpu_prefill(case), label="l2norm flag")
 
 
+@pytest.mark.parametrize("C,d", [(64, 128), (32, 64)])
+def test_prefill_strong_decay(C, d):
+    """Decay three times stronger than the workloads': chunk totals of the
+    log-decay pass -80 at C=64 (around it at C=32), so the Gram products take
+    per-sub-chunk reference points for some or all chunks."""
+    case = _varlen(90 + C, d, C, F32, g_scale=3.0, scale=inv_sqrt(d))
+    check_prefill(case, gpu_prefill(case), label=f"strong decay C={C} d={d}")
+
+
 def test_prefill_tiny_config():
     """1 sequence, T=64, H=2, d=16, C=16, fp32 everywhere, zero initial state."""
     case = wl.tiny_prefill()
