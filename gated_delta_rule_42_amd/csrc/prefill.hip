@@ -67,6 +67,17 @@ struct Shape {
     static constexpr int64_t OFF_A = OFF_U + D * BTP;          // Aqk  [BT][BTP]
     static constexpr int64_t BF16_END = OFF_A + BT * BTP;
     static constexpr int64_t EG_BYTE_OFF = BF16_END * 2;       // e^{G_C} fp32 [DKP]
+    // Aqk keeps only the columns its products read: token tile t stores
+    // columns 0 .. aq_width(t) - 1 (the 32-wide K steps up to its diagonal
+    // block), tiles one after another.
+    static constexpr int aq_width(int t) { return 32 * ((16 * t + 15) / 32 + 1); }
+    static constexpr int aq_base(int t)
+    {
+        int b = 0;
+        for (int i = 0; i < t; ++i) b += 16 * aq_width(i);
+        return b;
+    }
+    static constexpr int AQ_ELEMS = aq_base(NS);
     static constexpr int64_t REC_BYTES = ((EG_BYTE_OFF + DKP * 4) + 255) / 256 * 256;
     static_assert(BT % 16 == 0 && BT <= 64, "chunk size");
     static_assert(D % 16 == 0 && D <= 128, "head dim");
@@ -179,6 +190,18 @@ __device__ __forceinline__ int swz(int row, int col)
     else if constexpr (NC == 8) f = (row & 7) ^ ((row >> 3) & 1);
     else f = (row >> 2) & 3;
     return row * ROWLEN + (((col >> 3) ^ f) << 3) + (col & 7);
+}
+
+// Element offset of (row r, col) in the compact Aqk layout (aq_width above):
+// tile t = r / 16 holds 16 rows of 32 (t < 2) or 64 (t >= 2) columns, each row
+// swizzled like swz.
+__device__ __forceinline__ int aq_index(int r, int col)
+{
+    const int t = r >> 4;
+    const int w = t < 2 ? 32 : 64;
+    const int base = t == 0 ? 0 : t == 1 ? 512 : t == 2 ? 1024 : 2048;
+    const int f = w == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
+    return base + (r & 15) * w + ((((col >> 3) ^ f) & (w / 8 - 1)) << 3) + (col & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -483,10 +506,10 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                 aq[ii] = s <= r ? cq[ii] : 0.0f;
             }
             *reinterpret_cast<f32x4*>(&sM[r][16 * j + 4 * g4]) = mk;
-            *reinterpret_cast<bf16x4*>(wA + swz<BTP>(r, 16 * j + 4 * g4)) = pack_bf16x4(aq);
+            *reinterpret_cast<bf16x4*>(wA + aq_index(r, 16 * j + 4 * g4)) = pack_bf16x4(aq);
         }
-        for (int j = wave + 1; j < BTP / 16; ++j)   // above the diagonal (and padding)
-            *reinterpret_cast<bf16x4*>(wA + swz<BTP>(r, 16 * j + 4 * g4)) = bf16x4{};
+        for (int j = wave + 1; j < P::aq_width(wave) / 16; ++j)   // above the diagonal
+            *reinterpret_cast<bf16x4*>(wA + aq_index(r, 16 * j + 4 * g4)) = bf16x4{};
         // T is zero above the diagonal blocks (and in the token padding).
         for (int cc = 16 * (wave + 1) + 4 * g4; cc < BTP; cc += 16)
             *reinterpret_cast<bf16x4*>(&sT[r][cc]) = bf16x4{};
@@ -607,35 +630,37 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
 // ---------------------------------------------------------------------------
 // chain_kernel: the state-dependent part, serial over a sequence's chunks.
 //
-// One workgroup per (sequence, head, 16-column d_v tile) with thirteen waves
-// in four roles.  Each role runs its own loop over the chunks and every role
+// One workgroup per (sequence, head, 16-column d_v tile) with twelve waves
+// in three roles.  Each role runs its own loop over the chunks and every role
 // executes the same two barriers per chunk.  Phase 1 (before B1) reads S;
 // phase 2 (between B1 and B2) reads D and writes the next S:
 //   state waves 0-3    phase 1: D = U - W S for token tile w.
 //                      phase 2: S <- e^{G_C} S + Kb^T D for key tiles w, w+4.
 //                      S stays in fp32 accumulators and is shared as bf16 S^T.
 //   output waves 4-7   phase 1: Q~ S;  phase 2: + Aqk D, scaled and stored,
-//                      for token tile w-4.
+//                      for token tile w-4 (computed transposed, so each lane
+//                      stores 4 consecutive columns of one output row).
 //   loader waves 8-11  stream the record into two LDS rings with
-//                      asynchronous global->LDS loads: ring A (W, Q~, the U
+//                      asynchronous global->LDS copies: ring A (W, Q~, the U
 //                      tile; read in phase 1) with 2 stages and ring B (Kb^T,
 //                      Aqk, e^{G_C}; read in phase 2) with 3 stages.  A stage
 //                      is refilled as soon as the phase that reads it has
-//                      passed its barrier.
-//   warmer wave 12     asks for this tile's share of the record WARM chunks
-//                      ahead, so that the L2 of the XCD (shared by all tiles of
-//                      the pair) holds each record before it is streamed; a CU
-//                      reads its L2 several times faster than it pulls from HBM.
+//                      passed its barrier, in two halves spread over the two
+//                      phases.
+// The copies share the CU's path from L2 into LDS (about 64 bytes per clock,
+// which also bounds LDS writes); with ~57 KB per chunk it bounds the time per
+// chunk together with the two dependent phases.  The eight tiles of one
+// (sequence, head) are placed on one XCD by the grid order, so each record
+// comes from HBM into that XCD's L2 once.
 // Compute waves issue no global loads, and each loader wave owns one stream,
 // so no wave waits on another's prefetch (waits count per wave, in order).
-// The record's bf16 tiles are stored with swizzled 16-byte chunks (swz), so
-// the linear copies land in LDS in a layout that 16 lanes reading one chunk
-// column of 16 rows read without bank conflicts.
-constexpr int kChainWaves = 13;
+// The record's bf16 tiles are stored with swizzled 16-byte chunks (swz,
+// aq_index), so the linear copies land in LDS in a layout that 16 lanes
+// reading one chunk column of 16 rows read without bank conflicts.
+constexpr int kChainWaves = 12;
 constexpr int kChainThreads = kChainWaves * kWave;
 constexpr int kStagesA = 2;
 constexpr int kStagesB = 3;
-constexpr int kWarm = 4;
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int copy_ops(int bytes) { return (bytes + kWave * 16 - 1) / (kWave * 16); }
@@ -650,14 +675,21 @@ struct ChainRings {
     static constexpr int A_BYTES = round_up(U_OFF + 16 * P::BTP * 2, 512);
     // ring B stage
     static constexpr int KB_OFF = 0;                                  // Kb^T [DKP][BTP]
-    static constexpr int AQ_OFF = KB_OFF + P::DKP * P::BTP * 2;       // Aqk  [BT][BTP]
-    static constexpr int EG_OFF = AQ_OFF + BT * P::BTP * 2;           // e^{G_C} [DKP] fp32
+    static constexpr int AQ_OFF = KB_OFF + P::DKP * P::BTP * 2;       // Aqk, compact
+    static constexpr int EG_OFF = AQ_OFF + P::AQ_ELEMS * 2;           // e^{G_C} [DKP] fp32
     static constexpr int B_BYTES = round_up(EG_OFF + P::DKP * 4, 512);
     // asynchronous copies (1 KB each) per stage and loader wave
     static constexpr int OPS_L0 = copy_ops(BT * P::DKP * 2) + copy_ops(16 * P::BTP * 2);  // W, U
     static constexpr int OPS_L1 = copy_ops(BT * P::DKP * 2);                              // Q~
     static constexpr int OPS_L2 = copy_ops(P::DKP * P::BTP * 2);                          // Kb^T
-    static constexpr int OPS_L3 = copy_ops(BT * P::BTP * 2) + copy_ops(P::DKP * 4);       // Aqk, e^G
+    static constexpr int OPS_L3 = copy_ops(P::AQ_ELEMS * 2) + copy_ops(P::DKP * 4);       // Aqk, e^G
+    // the first of the two halves each loader issues per chunk
+    static constexpr int OPS_L0_H0 = copy_ops(BT * P::DKP);                               // W, first half
+    static constexpr int OPS_L1_H0 = copy_ops(BT * P::DKP);                               // Q~, first half
+    static constexpr int OPS_L2_H0 = copy_ops(P::DKP * P::BTP);                           // Kb^T, first half
+    static constexpr int OPS_L3_H0 = copy_ops(P::AQ_ELEMS * 2);                           // Aqk
+    static_assert(OPS_L0 + OPS_L0_H0 < 64 && OPS_L1 + OPS_L1_H0 < 64, "vmcnt range");
+    static_assert(2 * OPS_L2 + OPS_L2_H0 < 64 && 2 * OPS_L3 + OPS_L3_H0 < 64, "vmcnt range");
     static_assert(kStagesA * OPS_L0 < 64 && kStagesA * OPS_L1 < 64, "vmcnt range");
     static_assert(kStagesB * OPS_L2 < 64 && kStagesB * OPS_L3 < 64, "vmcnt range");
 };
@@ -686,7 +718,6 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
     using P = Shape<D, BT>;
     using R = ChainRings<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS;
-    constexpr int TILES = D / 16;                 // column tiles of one (sequence, head)
     constexpr int NKT_W = (P::NMT_K + 3) / 4;     // key m-tiles per state wave
     constexpr int SP = DKP + 8, DP = BTP + 8;     // bf16 pitches of the exchange tiles
 
@@ -694,7 +725,6 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kStagesB][R::B_BYTES];
     __shared__ __attribute__((aligned(16))) bf16 sS[16][SP];      // bf16 S^T of the tile
     __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // bf16 D^T
-    __shared__ __attribute__((aligned(1024))) uint8_t sWarm[kWave * 16];   // discarded
 
     // blockIdx.x enumerates (sequence, head) pairs, padded to a multiple of 8,
     // and blockIdx.y the column tile: workgroups are dealt to the 8 XCDs
@@ -824,6 +854,9 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
         }
     } else if (wave < 8) {
         // ---------------- output waves ----------------
+        // O^T = S^T Q~^T + D^T Aqk^T: with the operands of O = Q~ S + Aqk D
+        // swapped, lane l holds 4 consecutive columns of output row
+        // 16 tt + l % 16 and writes them with one vector store.
         const int tt = wave - 4;                   // token tile
         const bool active = tt < NS;
         const int kmax = (16 * tt + 15) / 32;      // Aqk is zero beyond the diagonal
@@ -836,10 +869,10 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
             if (active) {
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_K; ++kk) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + swz<DKP>(r, 32 * kk + 8 * g4));
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
-                    if (kk & 1) acc1 = mfma16x16x32(a, b, acc1);
-                    else acc0 = mfma16x16x32(a, b, acc0);
+                    const bf16x8 sf = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
+                    const bf16x8 qf = *reinterpret_cast<const bf16x8*>(sQ + swz<DKP>(r, 32 * kk + 8 * g4));
+                    if (kk & 1) acc1 = mfma16x16x32(sf, qf, acc1);
+                    else acc0 = mfma16x16x32(sf, qf, acc0);
                 }
             }
             lds_barrier();                         // B1
@@ -848,94 +881,80 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 for (int kk = 0; kk < P::NKK_T; ++kk)
                     if (kk <= kmax)
                         acc0 = mfma16x16x32(
-                            *reinterpret_cast<const bf16x8*>(sAq + swz<BTP>(r, 32 * kk + 8 * g4)),
-                            *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc0);
+                            *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]),
+                            *reinterpret_cast<const bf16x8*>(sAq + aq_index(r, 32 * kk + 8 * g4)), acc0);
                 const int64_t tc = s_begin + (int64_t)lc * BT;
-                const int clen = min(BT, len - lc * BT);
+                if (r < min(BT, len - lc * BT)) {
+                    float o4[4];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int rr = 16 * tt + 4 * g4 + ii;
-                    if (rr < clen)
-                        out[(tc + rr) * os + (int64_t)h * D + col] = from_f32<AT>(scale * (acc0[ii] + acc1[ii]));
+                    for (int ii = 0; ii < 4; ++ii) o4[ii] = scale * (acc0[ii] + acc1[ii]);
+                    store4(out + (tc + r) * os + (int64_t)h * D + n0 + 4 * g4, o4);
                 }
             }
             lds_barrier();                         // B2
         }
     } else if (wave < 10) {
         // ---------------- ring A loaders ----------------
-        // Stage lc % 2 is read in phase 1 of chunk lc; after B1 of chunk lc it
-        // is refilled with chunk lc + 2, which must be complete by B2 of
-        // chunk lc + 1.
+        // Stage lc % 2 is read in phase 1 of chunk lc.  Chunk lc + 2 goes
+        // into it in two halves, after B1 and after B2 of chunk lc, so that
+        // the copies are spread over both phases; chunk lc + 1 must be
+        // complete by B2 of chunk lc.
         const int lw = wave - 8;
-        auto issue = [&](int lc) {
+        auto issue = [&](int lc, int part) {
             uint8_t* dst = sA[lc % kStagesA];
             const uint8_t* rec = record(lc);
+            constexpr int HALF = BT * DKP;          // bytes: half of W or of Q~
             if (lw == 0) {
-                copy_async(dst + R::W_OFF, rec + P::OFF_W * 2, BT * DKP * 2, lane);
-                copy_async(dst + R::U_OFF, rec + (P::OFF_U + (int64_t)n0 * BTP) * 2, 16 * BTP * 2, lane);
+                copy_async(dst + R::W_OFF + part * HALF, rec + P::OFF_W * 2 + part * HALF, HALF, lane);
+                if (part)
+                    copy_async(dst + R::U_OFF, rec + (P::OFF_U + (int64_t)n0 * BTP) * 2, 16 * BTP * 2, lane);
             } else {
-                copy_async(dst + R::Q_OFF, rec + P::OFF_Q * 2, BT * DKP * 2, lane);
+                copy_async(dst + R::Q_OFF + part * HALF, rec + P::OFF_Q * 2 + part * HALF, HALF, lane);
             }
         };
-        issue(0);
-        issue(1);
+        issue(0, 0); issue(0, 1);
+        issue(1, 0); issue(1, 1);
         if (lw == 0) wait_vmcnt<R::OPS_L0>();      // chunk 0 complete
         else wait_vmcnt<R::OPS_L1>();
         lds_barrier();                             // B0
         for (int lc = 0; lc < nch; ++lc) {
             lds_barrier();                         // B1
-            issue(lc + 2);
-            if (lw == 0) wait_vmcnt<R::OPS_L0>();  // chunk lc + 1 complete
-            else wait_vmcnt<R::OPS_L1>();
+            issue(lc + 2, 0);
+            if (lw == 0) wait_vmcnt<R::OPS_L0_H0>();   // chunk lc + 1 complete
+            else wait_vmcnt<R::OPS_L1_H0>();
             lds_barrier();                         // B2
-        }
-        wait_vmcnt<0>();
-    } else if (wave < 12) {
-        // ---------------- ring B loaders ----------------
-        // Stage lc % 3 is read in phase 2 of chunk lc; after B2 of chunk lc it
-        // is refilled with chunk lc + 3.  Chunk lc must be complete by B1 of
-        // chunk lc, with chunks lc + 1 and lc + 2 still in flight.
-        const int lw = wave - 10;
-        auto issue = [&](int lc) {
-            uint8_t* dst = sB[lc % kStagesB];
-            const uint8_t* rec = record(lc);
-            if (lw == 0) {
-                copy_async(dst + R::KB_OFF, rec + P::OFF_KB * 2, DKP * BTP * 2, lane);
-            } else {
-                copy_async(dst + R::AQ_OFF, rec + P::OFF_A * 2, BT * BTP * 2, lane);
-                copy_async(dst + R::EG_OFF, rec + P::EG_BYTE_OFF, DKP * 4, lane);
-            }
-        };
-        issue(0);
-        issue(1);
-        issue(2);
-        lds_barrier();                             // B0
-        for (int lc = 0; lc < nch; ++lc) {
-            if (lw == 0) wait_vmcnt<2 * R::OPS_L2>();
-            else wait_vmcnt<2 * R::OPS_L3>();
-            lds_barrier();                         // B1
-            lds_barrier();                         // B2
-            issue(lc + 3);
+            issue(lc + 2, 1);
         }
         wait_vmcnt<0>();
     } else {
-        // ---------------- warmer wave ----------------
-        constexpr int SHARE = (int)((P::REC_BYTES + TILES - 1) / TILES / 16 * 16);
-        auto warm = [&](int lc) {
-            if (lc >= nch) return;                 // uniform
-            const uint8_t* base = record(lc) + (int64_t)tile * SHARE;
-            for (int off = 0; off < SHARE; off += kWave * 16) {
-                const int o = off + lane * 16;
-                if (o < SHARE && tile * SHARE + o + 16 <= P::REC_BYTES)
-                    __builtin_amdgcn_global_load_lds((const void*)(base + o), (lds_void*)sWarm, 16, 0, 0);
+        // ---------------- ring B loaders ----------------
+        // Stage lc % 3 is read in phase 2 of chunk lc.  Chunk lc + 3 goes
+        // into it in two halves, after B2 of chunk lc and after B1 of chunk
+        // lc + 1; chunk lc must be complete by B1 of chunk lc.
+        const int lw = wave - 10;
+        auto issue = [&](int lc, int part) {
+            uint8_t* dst = sB[lc % kStagesB];
+            const uint8_t* rec = record(lc);
+            if (lw == 0) {
+                constexpr int HALF = DKP * BTP;     // bytes: half of Kb^T
+                copy_async(dst + R::KB_OFF + part * HALF, rec + P::OFF_KB * 2 + part * HALF, HALF, lane);
+            } else if (part == 0) {
+                copy_async(dst + R::AQ_OFF, rec + P::OFF_A * 2, P::AQ_ELEMS * 2, lane);
+            } else {
+                copy_async(dst + R::EG_OFF, rec + P::EG_BYTE_OFF, DKP * 4, lane);
             }
         };
-        for (int lc = 2; lc < 2 + kWarm; ++lc) warm(lc);
+        issue(0, 0); issue(0, 1);
+        issue(1, 0); issue(1, 1);
+        issue(2, 0);
         lds_barrier();                             // B0
         for (int lc = 0; lc < nch; ++lc) {
-            warm(lc + 2 + kWarm);
+            if (lw == 0) wait_vmcnt<R::OPS_L2 + R::OPS_L2_H0>();   // chunk lc complete
+            else wait_vmcnt<R::OPS_L3 + R::OPS_L3_H0>();
             lds_barrier();                         // B1
+            issue(lc + 2, 1);
             lds_barrier();                         // B2
+            issue(lc + 3, 0);
         }
         wait_vmcnt<0>();
     }
