@@ -38,12 +38,12 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "d90032e7eb826ce155a3832b3a36f037db8ddc5faa00e165e0b57ac65d5e91c6",
-              88422752, 76022477),
-    "chain": (_PREFILL_SRC, "d90032e7eb826ce155a3832b3a36f037db8ddc5faa00e165e0b57ac65d5e91c6",
-              77311209, 17825792),
+    "intra": (_PREFILL_SRC, "f136a9f7806dcfb6a5b36955a9d09bd60590535c51e71a0175cbdb83b52dc51f",
+              88383210, 74113331),
+    "chain": (_PREFILL_SRC, "f136a9f7806dcfb6a5b36955a9d09bd60590535c51e71a0175cbdb83b52dc51f",
+              75168018, 18020864),
     "decode": (_DECODE_SRC, "793b8b75d03969d4e3dce510735401b11731f26dedb9d9d875c1cf3299173e77",
-               548207217, 538968064),
+               548211414, 538968064),
 }
 
 

@@ -323,26 +323,36 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     const int r = 16 * (tok_wave ? wave : 0) + l16;  // this lane's token row
     const bool valid = tok_wave && r < len;
 
-    // 0. Loads: this lane's token, channels 32 kk + 8 g4 .. + 7.
+    // 0. Loads: this lane's token, channels 32 kk + 8 g4 .. + 7, in the
+    //    order of first use (g for the scan, then k and q, v last) so each
+    //    phase waits only for what it reads.
     bf16x8 kq[NKK], kk8[NKK], kv[NKK];
     float gv[NKK][8];
     float b_r = 0.0f;
+    const int64_t tr = t0 + r;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         const int c0 = 32 * kk + 8 * g4;
         if (valid && c0 < D) {
-            const int64_t t = t0 + r;
-            kq[kk] = load8_bf16(q + t * qs + (int64_t)h * D + c0);
-            kk8[kk] = load8_bf16(k + t * ks + (int64_t)h * D + c0);
-            kv[kk] = load8_bf16(v + t * vs + (int64_t)h * D + c0);
-            load8(g + (t * heads + h) * D + c0, gv[kk]);
+            load8(g + (tr * heads + h) * D + c0, gv[kk]);
         } else {
-            kq[kk] = bf16x8{}; kk8[kk] = bf16x8{}; kv[kk] = bf16x8{};
 #pragma unroll
             for (int e = 0; e < 8; ++e) gv[kk][e] = 0.0f;
         }
     }
-    if (valid) b_r = beta[(t0 + r) * heads + h];
+    if (valid) b_r = beta[tr * heads + h];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const int c0 = 32 * kk + 8 * g4;
+        const bool ok = valid && c0 < D;
+        kk8[kk] = ok ? load8_bf16(k + tr * ks + (int64_t)h * D + c0) : bf16x8{};
+        kq[kk] = ok ? load8_bf16(q + tr * qs + (int64_t)h * D + c0) : bf16x8{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const int c0 = 32 * kk + 8 * g4;
+        kv[kk] = (valid && c0 < D) ? load8_bf16(v + tr * vs + (int64_t)h * D + c0) : bf16x8{};
+    }
     if (tok_wave && g4 == 0) sBeta[r] = b_r;
     if (BTP > BT && tid < BTP - BT) sBeta[BT + tid] = 0.0f;
 
