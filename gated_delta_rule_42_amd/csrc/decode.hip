@@ -15,7 +15,8 @@
 // The step is HBM-bound (0.87 flop per state byte): each workgroup streams
 // one head's state through registers exactly once -- read, update, write back
 // to the same address -- with every load of the state issued before any
-// arithmetic so the whole 64 KiB (fp32, d = 128) is in flight at once.
+// arithmetic so the whole 64 KiB (fp32, d = 128) is in flight at once.  The
+// state stream uses nontemporal loads and stores (touched once per step).
 //
 // Thread layout: TPR threads cover one state row (4 columns each, 16 B fp32 /
 // 8 B bf16 vectors); RG row groups; thread (rg, c) owns rows rg, rg+RG, ...
@@ -33,7 +34,7 @@ template <int DK, int DV>
 struct DecodeShape {
     static constexpr int CPT = 4;                                    // columns per thread
     static constexpr int TPR = DV / CPT;                             // threads per row
-    static constexpr int RG = (DK < 256 / TPR) ? DK : 256 / TPR;     // row groups
+    static constexpr int RG = (DK < 512 / TPR) ? DK : 512 / TPR;     // row groups
     static constexpr int NT = TPR * RG;                              // block size
     static constexpr int RPT = DK / RG;                              // rows per thread
     static_assert(DV % CPT == 0 && DK % RG == 0 && NT % kWave == 0, "decode shape");
@@ -70,7 +71,7 @@ void kda_decode_kernel(const AT* __restrict__ q, const AT* __restrict__ k,
     ST* S = pool + ((int64_t)slot * heads + h) * (int64_t)(DK * DV);
     float s[Sh::RPT][4];
 #pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) load4(S + (int64_t)(rg + i * Sh::RG) * DV + c0, s[i]);
+    for (int i = 0; i < Sh::RPT; ++i) load4_stream(S + (int64_t)(rg + i * Sh::RG) * DV + c0, s[i]);
 
     const int64_t bh = (int64_t)b * heads + h;
     for (int i = tid; i < DK; i += Sh::NT) {
@@ -138,7 +139,7 @@ void kda_decode_kernel(const AT* __restrict__ q, const AT* __restrict__ k,
         const float kr = s_k[r];
 #pragma unroll
         for (int c = 0; c < 4; ++c) s[i][c] += kr * d[c];
-        store4(S + (int64_t)r * DV + c0, s[i]);
+        store4_stream(S + (int64_t)r * DV + c0, s[i]);
     }
 }
 

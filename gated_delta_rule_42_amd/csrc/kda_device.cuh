@@ -49,6 +49,36 @@ __device__ __forceinline__ void store4(bf16* p, const float (&x)[4])
     *reinterpret_cast<bf16x4*>(p) = t;
 }
 
+// Streaming variants for data read once and written once (the recurrent
+// states of decode): nontemporal accesses keep the stream from being retained
+// in the caches, which raises the achieved HBM bandwidth of a read-modify-write
+// pass (measured on MI355X: 6.1 vs 5.4 TB/s for a 1 GiB in-place update).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void load4_stream(const float* p, float (&x)[4])
+{
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    x[0] = t[0]; x[1] = t[1]; x[2] = t[2]; x[3] = t[3];
+}
+__device__ __forceinline__ void load4_stream(const bf16* p, float (&x)[4])
+{
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    const bf16x4 b = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = static_cast<float>(b[i]);
+}
+__device__ __forceinline__ void store4_stream(float* p, const float (&x)[4])
+{
+    const f32x4 t = {x[0], x[1], x[2], x[3]};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store4_stream(bf16* p, const float (&x)[4])
+{
+    bf16x4 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = static_cast<bf16>(x[i]);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2, b), reinterpret_cast<u32x2*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Wave reductions (64 lanes).
 __device__ __forceinline__ float wave_sum(float x)
