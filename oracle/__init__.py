@@ -9,6 +9,8 @@ every result is fp64.
 Functions (all return new arrays; inputs are never modified):
   prefill(...)      token-by-token recurrence over a varlen batch      (kda_oracle.c)
   decode(...)       one recurrent step per row                         (kda_oracle.c)
+  spec_decode(...)  ntok draft tokens per row, state after each token  (kda_oracle.c)
+  spec_commit(...)  accept a prefix: copy its last state into the pool (kda_oracle.c)
   conv1d(...)       causal depthwise conv1d with rolling conv state    (kda_oracle.c)
   gated_rmsnorm(...) RMSNorm then SiLU gate                           (kda_oracle.c)
   chunk_form.*      the chunked algebra in fp64, a second algorithm used to pin
@@ -71,6 +73,16 @@ class Oracle:
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             _f64p, ctypes.c_int64, _i64p,
             ctypes.c_double, ctypes.c_int, ctypes.c_double, _f64p]
+        lib.kda_oracle_spec_decode.restype = ctypes.c_int
+        lib.kda_oracle_spec_decode.argtypes = [
+            _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _f64p, ctypes.c_int64, _i64p, _f64p,
+            ctypes.c_double, ctypes.c_int, ctypes.c_double, _f64p]
+        lib.kda_oracle_spec_commit.restype = ctypes.c_int
+        lib.kda_oracle_spec_commit.argtypes = [
+            _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _i64p, _f64p, ctypes.c_int64, _i64p]
         lib.kda_oracle_conv1d.restype = ctypes.c_int
         lib.kda_oracle_conv1d.argtypes = [
             _f64p, _f64p, _f64p, _f64p, ctypes.c_int64,
@@ -137,6 +149,44 @@ class Oracle:
             raise ValueError(f"kda_oracle_decode failed with status {rc}")
         return o, pool
 
+    def spec_decode(self, q, k, v, g, beta, pool, slots, ntok: int, scale: float = 1.0,
+                    l2norm_qk: bool = False, l2_eps: float = 1e-6):
+        """ntok draft tokens per row.  q,k,g [B*ntok,H,dk]; v [B*ntok,H,dv];
+        beta [B*ntok,H]; pool [slots,H,dk,dv] (not modified); slots [B].
+        Returns (o [B*ntok,H,dv], token_states [B,ntok,H,dk,dv]); token states
+        of padding rows are NaN (untouched)."""
+        q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
+        sl = _i64(slots)
+        pool = _f64(pool)
+        R, H, dk = q.shape
+        dv = v.shape[2]
+        B = sl.shape[0]
+        assert R == B * ntok and pool.shape[1:] == (H, dk, dv)
+        o = np.full((R, H, dv), np.nan)
+        ts = np.full((B, ntok, H, dk, dv), np.nan)
+        rc = self.lib.kda_oracle_spec_decode(
+            _ptr(q, _f64p), _ptr(k, _f64p), _ptr(v, _f64p), _ptr(g, _f64p), _ptr(beta, _f64p),
+            B, ntok, H, dk, dv, _ptr(pool, _f64p), pool.shape[0], _ptr(sl, _i64p),
+            _ptr(ts, _f64p), float(scale), int(bool(l2norm_qk)), float(l2_eps), _ptr(o, _f64p))
+        if rc != 0:
+            raise ValueError(f"kda_oracle_spec_decode failed with status {rc}")
+        return o, ts
+
+    def spec_commit(self, token_states, accepted, pool, slots):
+        """pool[slots[b]] = token_states[b, accepted[b]-1] where accepted[b] > 0.
+        Returns the new pool."""
+        ts = _f64(token_states)
+        acc, sl = _i64(accepted), _i64(slots)
+        pool = _f64(pool).copy()
+        B, ntok, H, dk, dv = ts.shape
+        assert acc.shape == (B,) and sl.shape == (B,) and pool.shape[1:] == (H, dk, dv)
+        rc = self.lib.kda_oracle_spec_commit(
+            _ptr(ts, _f64p), B, ntok, H, dk, dv, _ptr(acc, _i64p), _ptr(pool, _f64p),
+            pool.shape[0], _ptr(sl, _i64p))
+        if rc != 0:
+            raise ValueError(f"kda_oracle_spec_commit failed with status {rc}")
+        return pool
+
     def conv1d(self, x, w, cu_seqlens, conv_pool, slots, has_init=None, bias=None,
                silu: bool = True):
         """x [T,C]; w [C,W]; conv_pool [slots,W-1,C]. Returns (y, new conv pool)."""
@@ -195,6 +245,14 @@ def prefill(*args, **kwargs):
 
 def decode(*args, **kwargs):
     return default().decode(*args, **kwargs)
+
+
+def spec_decode(*args, **kwargs):
+    return default().spec_decode(*args, **kwargs)
+
+
+def spec_commit(*args, **kwargs):
+    return default().spec_commit(*args, **kwargs)
 
 
 def conv1d(*args, **kwargs):

@@ -255,6 +255,93 @@ int kda_oracle_decode(const double* q, const double* k, const double* v,
  *   conv_pool : [n_slots, W-1, Cch], row W-2 is the most recent input
  *   slots : [n_seqs]; < 0 marks padding (zero output, no state I/O)
  */
+/*
+ * Speculative multi-token decode (page "[Feature][KDA] Add Kimi K3 KDA
+ * execution", Metadata construction: speculative decode is a path of its own
+ * next to prefill and decode; page "FlashKDA kernel upgrade supports bf16
+ * checkpoint state", risks: restoring checkpoint states in the speculative
+ * decode chain).
+ *
+ * Reading taken: row b carries ntok draft tokens, rows b*ntok + t (t in
+ * order) of the token arrays.  Starting from pool[slots[b]] the tokens are
+ * applied one by one with the recurrence above; the output of token t is
+ * o[b*ntok + t] and the state after token t is stored in
+ * token_states[b, t] ([B, ntok, H, dk, dv]).  The pool is not modified, so
+ * the verifier can later accept any prefix (kda_oracle_spec_commit).
+ * slots[b] < 0: zero outputs, token states untouched.
+ */
+int kda_oracle_spec_decode(const double* q, const double* k, const double* v,
+                           const double* g, const double* beta, int64_t B, int64_t ntok,
+                           int64_t H, int64_t dk, int64_t dv,
+                           const double* pool, int64_t n_slots, const int64_t* slots,
+                           double* token_states, double scale, int l2norm_qk, double l2_eps,
+                           double* o)
+{
+    if (B < 0 || ntok < 0 || H <= 0 || dk <= 0 || dv <= 0) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+        if (slots[b] >= n_slots) return ORACLE_EINVAL;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(static)
+    for (int64_t unit = 0; unit < B * H; ++unit) {
+        const int64_t b = unit / H, h = unit % H;
+        if (slots[b] < 0) {
+            for (int64_t t = 0; t < ntok; ++t)
+                memset(o + ((b * ntok + t) * H + h) * dv, 0, (size_t)dv * sizeof(double));
+            continue;
+        }
+        double* S = (double*)malloc((size_t)(dk * dv) * sizeof(double));
+        double* work = (double*)malloc((size_t)dv * sizeof(double));
+        double* qn = (double*)malloc((size_t)dk * sizeof(double));
+        double* kn = (double*)malloc((size_t)dk * sizeof(double));
+        if (!S || !work || !qn || !kn) {
+            free(S); free(work); free(qn); free(kn);
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+            continue;
+        }
+        memcpy(S, pool + (slots[b] * H + h) * dk * dv, (size_t)(dk * dv) * sizeof(double));
+        for (int64_t t = 0; t < ntok; ++t) {
+            const int64_t row = b * ntok + t;
+            const double* qt = q + (row * H + h) * dk;
+            const double* kt = k + (row * H + h) * dk;
+            if (l2norm_qk) {
+                l2_normalise(qt, dk, l2_eps, qn);
+                l2_normalise(kt, dk, l2_eps, kn);
+                qt = qn;
+                kt = kn;
+            }
+            kda_token(S, dk, dv, qt, kt, v + (row * H + h) * dv, g + (row * H + h) * dk,
+                      beta[row * H + h], scale, o + (row * H + h) * dv, work);
+            memcpy(token_states + ((b * ntok + t) * H + h) * dk * dv, S,
+                   (size_t)(dk * dv) * sizeof(double));
+        }
+        free(S); free(work); free(qn); free(kn);
+    }
+    return status;
+}
+
+/*
+ * Commit the verifier's decision (same passages): for each row b with
+ * accepted[b] > 0, pool[slots[b]] = token_states[b, accepted[b] - 1]; rows
+ * with accepted[b] == 0 or slots[b] < 0 leave the pool alone.
+ */
+int kda_oracle_spec_commit(const double* token_states, int64_t B, int64_t ntok, int64_t H,
+                           int64_t dk, int64_t dv, const int64_t* accepted,
+                           double* pool, int64_t n_slots, const int64_t* slots)
+{
+    if (B < 0 || ntok < 0 || H <= 0 || dk <= 0 || dv <= 0) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+        if (slots[b] >= n_slots || accepted[b] < 0 || accepted[b] > ntok) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < B; ++b) {
+        if (slots[b] < 0 || accepted[b] == 0) continue;
+        for (int64_t h = 0; h < H; ++h)
+            memcpy(pool + (slots[b] * H + h) * dk * dv,
+                   token_states + ((b * ntok + accepted[b] - 1) * H + h) * dk * dv,
+                   (size_t)(dk * dv) * sizeof(double));
+    }
+    return ORACLE_OK;
+}
+
 int kda_oracle_conv1d(const double* x, const double* w, const double* bias,
                       double* conv_pool, int64_t n_slots,
                       const int64_t* cu_seqlens, const int64_t* slots,

@@ -327,7 +327,48 @@ def pin_rmsnorm_library(orc):
            1e-14, "constant rows: c / sqrt(c^2 + eps) * silu(gate)")
 
 
+def pin_spec_decode(orc):
+    """Speculative decode: row b's ntok tokens from pool[slot_b], state after
+    each token, pool untouched; commit copies an accepted prefix's state."""
+    rng = np.random.default_rng(113)
+    B, ntok, H, dk, dv = 4, 3, 2, 5, 4
+    q, k, v, g, beta = _rand_case(rng, B * ntok, H, dk, dv)
+    pool = rng.standard_normal((6, H, dk, dv))
+    slots = np.array([4, -1, 0, 2])
+    o, ts = orc.spec_decode(q, k, v, g, beta, pool, slots, ntok, scale=0.8)
+    # Closed form with beta = 0: pure decay, outputs read the decayed state.
+    o0, ts0 = orc.spec_decode(q, k, v, g, np.zeros_like(beta), pool, slots, ntok, scale=0.8)
+    for b in (0, 2, 3):
+        G = np.cumsum(g[b * ntok:(b + 1) * ntok], axis=0)        # [ntok, H, dk]
+        S0 = pool[slots[b]]
+        for t in range(ntok):
+            _close(ts0[b, t], np.exp(G[t])[:, :, None] * S0, 1e-13, "spec beta=0 state")
+            _close(o0[b * ntok + t], 0.8 * np.einsum("hkv,hk->hv", S0, np.exp(G[t]) * q[b * ntok + t]),
+                   1e-13, "spec beta=0 output")
+    # The same tokens as a varlen prefill of ntok-token sequences with a
+    # checkpoint after every token (a different indexing path).
+    cu = np.arange(0, B * ntok + 1, ntok)
+    op, _, ck = orc.prefill(q, k, v, g, beta, cu, pool, slots, ckpt_interval=1, scale=0.8)
+    real = [b for b in range(B) if slots[b] >= 0]
+    rows = np.concatenate([np.arange(b * ntok, (b + 1) * ntok) for b in real])
+    _close(o[rows], op[rows], 1e-14, "spec outputs vs prefill")
+    for b in real:
+        _close(ts[b], ck[b * ntok:(b + 1) * ntok], 1e-14, "spec token states vs checkpoints")
+    _close(o[ntok:2 * ntok], np.zeros((ntok, H, dv)), 0.0, "spec padding rows are zero")
+    assert np.isnan(ts[1]).all(), "padding rows leave their token states alone"
+    # Commit: accepted prefix lengths 2, -, 0, 3.
+    acc = np.array([2, 1, 0, 3])
+    p2 = orc.spec_commit(ts, acc, pool, slots)
+    _close(p2[4], ts[0, 1], 0.0, "commit copies the last accepted state")
+    _close(p2[2], ts[3, 2], 0.0, "commit of a full acceptance")
+    keep = [s for s in range(6) if s not in (4, 2)]
+    _close(p2[keep], pool[keep], 0.0, "zero acceptance, padding and other slots unchanged")
+    # Accepting n tokens equals prefilling those n tokens from the same state.
+    _, pp, _ = orc.prefill(q[0:2], k[0:2], v[0:2], g[0:2], beta[0:2], [0, 2], pool, [4])
+    _close(p2[4], pp[4], 1e-14, "commit of 2 tokens vs a 2-token prefill")
+
+
 ALL_PINS = [pin_hand_worked, pin_beta_zero, pin_exact_retrieval, pin_delta_invariant,
             pin_linearity, pin_chunk_form, pin_split_calls, pin_checkpoints, pin_decode,
             pin_padding_empty, pin_has_init, pin_l2norm, pin_conv_numpy, pin_conv_state,
-            pin_rmsnorm_library]
+            pin_rmsnorm_library, pin_spec_decode]

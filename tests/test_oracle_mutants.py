@@ -58,6 +58,18 @@ MUTANTS = {
     "conv_state_not_updated": _sub("memcpy(st, ext + L * Cch,", "if (0) memcpy(st, ext + L * Cch,"),
     "conv_state_ignored": _sub("if (!has_init || has_init[i]) memcpy(ext, st,",
                                "if (0) memcpy(ext, st,"),
+    "spec_state_saved_before_token": _sub(
+        "            kda_token(S, dk, dv, qt, kt, v + (row * H + h) * dv, g + (row * H + h) * dk,\n"
+        "                      beta[row * H + h], scale, o + (row * H + h) * dv, work);\n"
+        "            memcpy(token_states + ((b * ntok + t) * H + h) * dk * dv, S,\n"
+        "                   (size_t)(dk * dv) * sizeof(double));",
+        "            memcpy(token_states + ((b * ntok + t) * H + h) * dk * dv, S,\n"
+        "                   (size_t)(dk * dv) * sizeof(double));\n"
+        "            kda_token(S, dk, dv, qt, kt, v + (row * H + h) * dv, g + (row * H + h) * dk,\n"
+        "                      beta[row * H + h], scale, o + (row * H + h) * dv, work);"),
+    "spec_token_rows_interleaved": _sub("const int64_t row = b * ntok + t;", "const int64_t row = t * B + b;"),
+    "spec_commit_takes_last_draft": _sub("token_states + ((b * ntok + accepted[b] - 1) * H + h)",
+                                         "token_states + ((b * ntok + ntok - 1) * H + h)"),
     "rmsnorm_sum_not_mean": _sub("ss / (double)dim + eps", "ss + eps"),
     "rmsnorm_sigmoid_not_silu": _sub("double act = z / (1.0 + exp(-z));",
                                      "double act = 1.0 / (1.0 + exp(-z));"),
