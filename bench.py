@@ -11,6 +11,8 @@ on both sides.  To keep the inputs coming from HBM rather than from the 256 MB
 last-level cache, the calls rotate over four independent copies of the
 activations (each ~80 MB).  The same line carries:
   * decode: seq/s for 512 sequences x 1 token on an fp32 pool of 1024 slots;
+  * spec: speculative decode of the same batch with 4 draft tokens per row
+    (draft tokens/s; state after every token written), and its commit;
   * pipeline: tokens/s of one 4096-token call of the long-context pipeline
     (conv1d -> prefill with q/k L2 norm, bf16 state, checkpoint -> gated RMSNorm);
   * roofline objects (algorithmic bytes / measured time against 8 TB/s);
@@ -163,6 +165,40 @@ def bench_decode(steps: int, warmup: int):
     return case, ms, wall
 
 
+def spec_alg_bytes(B: int, ntok: int, H: int, dk: int, dv: int, act_bytes: int,
+                   state_bytes: int) -> int:
+    """Each row's state read once, one state written per draft token, and the
+    draft tokens' activations (q, k, v, o, g, beta)."""
+    per_token_head = (2 * dk + 2 * dv) * act_bytes + 4 * dk + 4
+    return B * H * (dk * dv * state_bytes * (1 + ntok) + ntok * per_token_head)
+
+
+def bench_spec(steps: int, warmup: int):
+    import torch
+    from gated_delta_rule_42_amd import kda, workloads as wl
+    case = wl.spec_batch()
+    dev = "cuda"
+    q, k, v, g, beta = (t.to(dev) for t in (case.q, case.k, case.v, case.g, case.beta))
+    pool = case.pool.to(dev)
+    slots = case.slots.to(dev)
+    B, ntok = case.slots.numel(), case.ntok
+    H, d = case.q.shape[1], case.q.shape[2]
+    ts = torch.empty(B, ntok, H, d, d, dtype=pool.dtype, device=dev)
+    out = torch.empty_like(v)
+
+    def call(i):
+        kda.spec_decode(q, k, v, g, beta, pool, slots, ts, out)
+
+    ms, wall, _ = time_calls(call, steps, warmup)
+    acc = case.accepted.to(dev)
+
+    def commit(i):
+        kda.spec_commit(ts, acc, pool, slots)
+
+    cms, _, _ = time_calls(commit, steps, warmup)
+    return case, ms, cms
+
+
 def bench_pipeline(steps: int, warmup: int):
     import torch
     from gated_delta_rule_42_amd import kda, workloads as wl
@@ -238,7 +274,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "pipeline", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "spec", "pipeline", "copy"],
+                    default=None,
                     help="run one leg only (for profiling); prints that leg's numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -292,6 +329,23 @@ def main() -> int:
             "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": dgbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
                          "traffic": traffic_bytes("decode"), "alg_bytes": dbytes}}
+    if args.only in (None, "spec"):
+        scase, sms, cms = bench_spec(K, W)
+        B, ntok, H, d = scase.slots.numel(), scase.ntok, 16, 128
+        sbytes = spec_alg_bytes(B, ntok, H, d, d, 2, 4)
+        n_acc = int((scase.accepted > 0).sum())
+        cbytes = 2 * n_acc * H * d * d * 4
+        result["spec"] = {
+            "value": B * ntok / (sms * 1e-3), "unit": "draft tokens/s", "ms_per_step": sms,
+            "steps": K, "workload": scase.name,
+            "roofline": {"kernel": "kda_decode_kernel (speculative, 4 tokens per row)",
+                         "bound": "hbm", "achieved": sbytes / (sms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None, "alg_bytes": sbytes},
+            "commit": {"ms_per_step": cms, "rows_accepting": n_acc,
+                       "achieved": cbytes / (cms * 1e-3) / 1e9, "unit": "GB/s",
+                       "alg_bytes": cbytes}}
     if args.only in (None, "pipeline"):
         lc, pms, pwall = bench_pipeline(K, W)
         result["pipeline"] = {

@@ -193,12 +193,76 @@ kda_status_t kda_recurrent_decode(
     a.q = q; a.k = k; a.v = v;
     a.q_stride = q_stride_b; a.k_stride = k_stride_b; a.v_stride = v_stride_b;
     a.g = g; a.beta = beta;
-    a.batch = batch; a.heads = num_heads; a.dk = dk; a.dv = dv;
+    a.batch = batch; a.ntok = 1; a.heads = num_heads; a.dk = dk; a.dv = dv;
     a.pool = state_pool; a.num_slots = num_slots; a.slots = state_indices;
+    a.token_states = nullptr;
     a.scale = scale; a.flags = flags;
     a.out = out; a.out_stride = out_stride_b;
     a.act = act_dtype; a.state = state_dtype;
     return launch_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_spec_decode(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    int32_t batch, int32_t ntok, int32_t num_heads, int32_t dk, int32_t dv,
+    const void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, void* token_states, float scale, uint32_t flags,
+    void* out, int64_t out_stride_t, void* stream)
+{
+    if (batch < 0 || ntok <= 0 || num_heads <= 0 || num_slots < 0) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(act_dtype) || !dtype_ok(state_dtype)) return KDA_ERR_INVALID_ARG;
+    if (flags & ~KDA_FLAG_QK_L2NORM) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || dk != dv) return KDA_ERR_UNSUPPORTED;
+    if (batch == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state_indices || !out || !token_states)
+        return KDA_ERR_INVALID_ARG;
+    if (num_slots > 0 && !state_pool) return KDA_ERR_INVALID_ARG;
+    const int64_t hk = (int64_t)num_heads * dk, hv = (int64_t)num_heads * dv;
+    if (q_stride_t < hk || k_stride_t < hk || v_stride_t < hv || out_stride_t < hv)
+        return KDA_ERR_INVALID_ARG;
+    if ((q_stride_t | k_stride_t | v_stride_t | out_stride_t) & 7) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(state_pool) || !aligned16(token_states))
+        return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * num_heads > INT32_MAX || (int64_t)batch * ntok > INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.q_stride = q_stride_t; a.k_stride = k_stride_t; a.v_stride = v_stride_t;
+    a.g = g; a.beta = beta;
+    a.batch = batch; a.ntok = ntok; a.heads = num_heads; a.dk = dk; a.dv = dv;
+    a.pool = const_cast<void*>(state_pool); a.num_slots = num_slots; a.slots = state_indices;
+    a.token_states = token_states;
+    a.scale = scale; a.flags = flags;
+    a.out = out; a.out_stride = out_stride_t;
+    a.act = act_dtype; a.state = state_dtype;
+    return launch_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_spec_commit(
+    const void* token_states, int32_t batch, int32_t ntok, int32_t num_heads,
+    int32_t dk, int32_t dv, const int32_t* num_accepted,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, void* stream)
+{
+    if (batch < 0 || ntok <= 0 || num_heads <= 0 || num_slots < 0) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(state_dtype)) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || dk != dv) return KDA_ERR_UNSUPPORTED;
+    if (batch == 0 || num_slots == 0) return KDA_OK;
+    if (!token_states || !num_accepted || !state_pool || !state_indices) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(token_states) || !aligned16(state_pool)) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+
+    kda::SpecCommitArgs a;
+    a.token_states = token_states;
+    a.batch = batch; a.ntok = ntok; a.heads = num_heads; a.dk = dk; a.dv = dv;
+    a.accepted = num_accepted;
+    a.pool = state_pool; a.num_slots = num_slots; a.slots = state_indices;
+    a.state = state_dtype;
+    return launch_status(kda::launch_spec_commit(a, static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_gated_rmsnorm(

@@ -10,18 +10,32 @@
 
 namespace kda {
 
+// Decode (ntok = 1, token_states null: the pool slot is updated in place)
+// and speculative decode (ntok >= 1 tokens per row, the state after each
+// token written to token_states; the pool is only read).
 struct DecodeArgs {
     const void* q; const void* k; const void* v;
-    int64_t q_stride, k_stride, v_stride;       // elements between rows
+    int64_t q_stride, k_stride, v_stride;       // elements between token rows
     const float* g; const float* beta;
-    int32_t batch, heads, dk, dv;
+    int32_t batch, ntok, heads, dk, dv;
     void* pool; int64_t num_slots;
     const int32_t* slots;
+    void* token_states;
     float scale; uint32_t flags;
     void* out; int64_t out_stride;
     kda_dtype_t act, state;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct SpecCommitArgs {
+    const void* token_states;
+    int32_t batch, ntok, heads, dk, dv;
+    const int32_t* accepted;
+    void* pool; int64_t num_slots;
+    const int32_t* slots;
+    kda_dtype_t state;
+};
+hipError_t launch_spec_commit(const SpecCommitArgs& a, hipStream_t stream);
 
 struct PrefillArgs {
     const void* q; const void* k; const void* v;

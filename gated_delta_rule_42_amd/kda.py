@@ -64,6 +64,12 @@ def _load() -> ctypes.CDLL:
     lib.kda_causal_conv1d.restype = i32
     lib.kda_causal_conv1d.argtypes = [
         vp, i64, vp, vp, vp, i64, vp, vp, vp, i32, i64, i32, i32, i32, u32, vp, i64, vp]
+    lib.kda_spec_decode.restype = i32
+    lib.kda_spec_decode.argtypes = [
+        vp, vp, vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, i32, i32,
+        vp, i32, i64, vp, vp, f32, u32, vp, i64, vp]
+    lib.kda_spec_commit.restype = i32
+    lib.kda_spec_commit.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i32, i64, vp, vp]
     lib.kda_prefill_timing_begin.restype = i32
     lib.kda_prefill_timing_begin.argtypes = [i32]
     lib.kda_prefill_timing_end.restype = i32
@@ -186,6 +192,50 @@ def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, out, *, scale:
         _ptr(state_indices), float(scale), int(flags), _ptr(out), _token_stride(out, "out"),
         _stream(stream))
     _check("kda_recurrent_decode", status)
+
+
+def spec_decode(q, k, v, g, beta, state_pool, state_indices, token_states, out, *,
+                scale: float = 1.0, flags: int = 0, stream=None) -> None:
+    """kda_spec_decode.  q,k [B*ntok,H,dk]; v,out [B*ntok,H,dv]; g [B*ntok,H,dk]
+    fp32; beta [B*ntok,H] fp32; state_pool read only; token_states
+    [B,ntok,H,dk,dv] with the pool's dtype (written)."""
+    R, H, dk = q.shape
+    dv = v.shape[2]
+    B = state_indices.numel()
+    if B == 0:
+        return
+    if R % B:
+        raise ValueError("token rows must be batch * ntok")
+    ntok = R // B
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    _contig(state_indices, "state_indices", torch.int32)
+    if not state_pool.is_contiguous():
+        raise ValueError("state_pool must be contiguous")
+    if (not token_states.is_contiguous() or token_states.dtype != state_pool.dtype
+            or tuple(token_states.shape) != (B, ntok, H, dk, dv)):
+        raise ValueError("token_states must be contiguous [B, ntok, H, dk, dv] in the pool dtype")
+    status = _lib.kda_spec_decode(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q),
+        _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v"),
+        _ptr(g), _ptr(beta), B, ntok, H, dk, dv,
+        _ptr(state_pool), _dtype(state_pool), state_pool.shape[0],
+        _ptr(state_indices), _ptr(token_states), float(scale), int(flags),
+        _ptr(out), _token_stride(out, "out"), _stream(stream))
+    _check("kda_spec_decode", status)
+
+
+def spec_commit(token_states, num_accepted, state_pool, state_indices, *, stream=None) -> None:
+    """kda_spec_commit: pool[slot_b] = token_states[b, num_accepted[b] - 1]."""
+    B, ntok, H, dk, dv = token_states.shape
+    _contig(num_accepted, "num_accepted", torch.int32)
+    _contig(state_indices, "state_indices", torch.int32)
+    if not state_pool.is_contiguous() or state_pool.dtype != token_states.dtype:
+        raise ValueError("state_pool must be contiguous with the token states' dtype")
+    status = _lib.kda_spec_commit(
+        _ptr(token_states), B, ntok, H, dk, dv, _ptr(num_accepted), _ptr(state_pool),
+        _dtype(state_pool), state_pool.shape[0], _ptr(state_indices), _stream(stream))
+    _check("kda_spec_commit", status)
 
 
 def gated_rmsnorm(x, gate, y, *, weight=None, eps: float = 1e-6, stream=None) -> None:

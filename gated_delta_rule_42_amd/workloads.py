@@ -198,6 +198,50 @@ def random_decode(seed: int, B: int, H: int, dk: int, dv: int, *, act_dtype=BF16
     return DecodeCase(name, q, k, v, g, beta, pool, torch.from_numpy(slots), scale, l2norm_qk)
 
 
+@dataclass
+class SpecCase:
+    """Speculative decode: ntok draft tokens for each of B rows."""
+    name: str
+    q: torch.Tensor            # [B*ntok, H, dk]
+    k: torch.Tensor
+    v: torch.Tensor            # [B*ntok, H, dv]
+    g: torch.Tensor            # [B*ntok, H, dk] fp32
+    beta: torch.Tensor         # [B*ntok, H] fp32
+    pool: torch.Tensor         # [n_slots, H, dk, dv]
+    slots: torch.Tensor        # [B] int32, < 0 = padding row
+    accepted: torch.Tensor     # [B] int32 in [0, ntok]: a verifier's decision
+    ntok: int
+    scale: float = 1.0
+    l2norm_qk: bool = False
+
+
+def random_spec(seed: int, B: int, ntok: int, H: int, dk: int, dv: int, *, act_dtype=BF16,
+                state_dtype=F32, n_slots: int | None = None, slots=None, scale: float = 1.0,
+                state_std: float = 0.02, qk_unit: bool = True, l2norm_qk: bool = False,
+                name: str = "random_spec") -> SpecCase:
+    """B rows of ntok draft tokens (rows b*ntok + t), slots a random
+    permutation prefix, accepted prefix lengths uniform in [0, ntok]."""
+    rng = np.random.default_rng(seed)
+    if n_slots is None:
+        n_slots = 2 * B
+    if slots is None:
+        slots = rng.permutation(n_slots)[:B]
+    slots = np.asarray(slots, dtype=np.int32)
+    q, k, v, g, beta = _draw_tokens(rng, B * ntok, H, dk, dv, act_dtype, qk_unit)
+    pool = _draw_pool(rng, n_slots, H, dk, dv, state_dtype, state_std)
+    accepted = rng.integers(0, ntok + 1, B).astype(np.int32)
+    return SpecCase(name, q, k, v, g, beta, pool, torch.from_numpy(slots),
+                    torch.from_numpy(accepted), ntok, scale, l2norm_qk)
+
+
+def spec_batch(seed: int = 6) -> SpecCase:
+    """512 rows x 4 draft tokens, H=16, d=128, bf16 q/k/v, fp32 pool of 1024
+    slots indexed by a random permutation (the decode batch, speculating 4
+    tokens)."""
+    return random_spec(seed, 512, 4, 16, 128, 128, n_slots=1024,
+                       name="spec_B512_ntok4_H16_d128_bf16_f32pool1024")
+
+
 def decode_batch(seed: int = 4) -> DecodeCase:
     """512 sequences x 1 token, H=16, d=128, bf16 q/k/v, fp32 pool of 1024
     slots indexed by a random permutation."""

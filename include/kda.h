@@ -217,6 +217,53 @@ kda_status_t kda_causal_conv1d(
     void* y, int64_t y_stride_t, void* stream);
 
 /*
+ * Speculative multi-token decode (page "[Feature][KDA] Add Kimi K3 KDA
+ * execution", Metadata construction: speculative decode is a path of its own
+ * next to chunk prefill and recurrent decode; page "FlashKDA kernel upgrade
+ * supports bf16 checkpoint state", risks: restoring checkpoint states in the
+ * speculative decode chain).
+ *
+ * Row b carries ntok draft tokens, token rows b*ntok + t (t = 0 .. ntok-1) in
+ * order.  Starting from state_pool[state_indices[b]], the tokens are applied
+ * with the recurrence at the top of this header; out[b*ntok + t] is the output
+ * of token t, and the state after token t is written to token_states[b, t].
+ * The pool is read and never written, so a verifier can accept any prefix
+ * afterwards with kda_spec_commit.
+ *   q, k     [batch*ntok, heads, dk] of act_dtype, token strides in elements
+ *   v, out   [batch*ntok, heads, dv] of act_dtype
+ *   g        [batch*ntok, heads, dk] fp32;  beta [batch*ntok, heads] fp32
+ *   state_pool [num_slots, heads, dk, dv] of state_dtype (read only)
+ *   state_indices [batch]; < 0 = padding row: zero outputs, its token states
+ *            are not written
+ *   token_states [batch, ntok, heads, dk, dv] of state_dtype (written)
+ *   flags    KDA_FLAG_QK_L2NORM
+ * Supported: dk = dv in {16, 32, 64, 128}, ntok >= 1.
+ */
+kda_status_t kda_spec_decode(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    int32_t batch, int32_t ntok, int32_t num_heads, int32_t dk, int32_t dv,
+    const void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, void* token_states, float scale, uint32_t flags,
+    void* out, int64_t out_stride_t, void* stream);
+
+/*
+ * Commit a verified speculative step (same passages): for every row b with
+ * state_indices[b] >= 0 and 0 < num_accepted[b] <= ntok,
+ * state_pool[state_indices[b]] = token_states[b, num_accepted[b] - 1], in
+ * place; rows with num_accepted[b] == 0 keep their state.  num_accepted is a
+ * device array of int32 [batch]; a value outside [0, ntok] is a caller
+ * contract violation and leaves that slot unchanged.  token_states and the
+ * pool must not overlap.
+ */
+kda_status_t kda_spec_commit(
+    const void* token_states, int32_t batch, int32_t ntok, int32_t num_heads,
+    int32_t dk, int32_t dv, const int32_t* num_accepted,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, void* stream);
+
+/*
  * Per-kernel timing of kda_chunk_prefill (a benchmarking aid; not part of the
  * operator).  The prefill is two kernels on the call's stream: the
  * intra-chunk kernel (every chunk in parallel) and the chain kernel (the

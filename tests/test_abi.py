@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_chunk_prefill", "kda_recurrent_decode", "kda_gated_rmsnorm",
                  "kda_causal_conv1d", "kda_chunk_prefill_workspace_size",
+                 "kda_spec_decode", "kda_spec_commit",
                  "kda_abi_version", "kda_status_string"):
         assert want in names
 
@@ -122,6 +123,39 @@ def test_decode_validation(lib):
     assert call(pool=FAKE + 4) == K.KDA_ERR_INVALID_ARG
     assert call(sdt=3) == K.KDA_ERR_INVALID_ARG
     assert call(flags=2) == K.KDA_ERR_INVALID_ARG
+
+
+def test_spec_decode_and_commit_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+
+    def spec(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, act=1, qs=2048, ks=2048, vs=2048, g=FAKE, beta=FAKE,
+                 B=4, ntok=3, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=8, idx=FAKE,
+                 ts=FAKE, scale=1.0, flags=0, out=FAKE, os=2048, stream=None)
+        a.update(over)
+        return lib.kda_spec_decode(*a.values())
+
+    assert spec(B=0) == K.KDA_OK
+    assert spec(ntok=0) == K.KDA_ERR_INVALID_ARG
+    assert spec(ts=None) == K.KDA_ERR_INVALID_ARG
+    assert spec(ts=FAKE + 8) == K.KDA_ERR_INVALID_ARG
+    assert spec(dk=48, dv=48) == K.KDA_ERR_UNSUPPORTED
+    assert spec(qs=1000) == K.KDA_ERR_INVALID_ARG
+    assert spec(flags=4) == K.KDA_ERR_INVALID_ARG
+
+    def commit(**over):
+        a = dict(ts=FAKE, B=4, ntok=3, H=16, dk=128, dv=128, acc=FAKE, pool=FAKE, sdt=1,
+                 slots=8, idx=FAKE, stream=None)
+        a.update(over)
+        return lib.kda_spec_commit(*a.values())
+
+    assert commit(B=0) == K.KDA_OK
+    assert commit(slots=0) == K.KDA_OK
+    assert commit(acc=None) == K.KDA_ERR_INVALID_ARG
+    assert commit(ntok=0) == K.KDA_ERR_INVALID_ARG
+    assert commit(sdt=5) == K.KDA_ERR_INVALID_ARG
+    assert commit(dk=128, dv=64) == K.KDA_ERR_UNSUPPORTED
+    assert commit(pool=FAKE + 2) == K.KDA_ERR_INVALID_ARG
 
 
 def test_norm_and_conv_validation(lib):
