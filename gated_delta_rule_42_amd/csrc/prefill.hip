@@ -174,34 +174,27 @@ __device__ __forceinline__ bf16x4 pack_bf16x4(const f32x4& x)
     return r;
 }
 
-// Element offset of (row, col) in a row-major bf16 tile with ROWLEN elements
-// per row whose 16-byte chunks are permuted within each row by an XOR of the
-// row index.  16 lanes reading the same logical chunk of 16 consecutive rows
-// then touch 16 distinct bank groups whether the LDS has 32 or 64 banks.  The
-// workspace records are written in this layout and copied byte for byte into
-// LDS.
-template <int ROWLEN>
-__device__ __forceinline__ int swz(int row, int col)
+// Element offset of (row, col) in a record tile with COLS columns stored as
+// MFMA operand fragments: the 16 x 32 block (row / 16, col / 32) is
+// fragment row / 16 * COLS / 32 + col / 32, 512 elements long, and lane
+// l = row % 16 + 16 ((col % 32) / 8) of it holds the 8 elements of that row
+// from column col & ~7 at element 8 l.  The wave that reads a 16 x 32
+// operand block of the tile then reads 1 KB of consecutive bytes.
+template <int COLS>
+__device__ __forceinline__ int frag(int row, int col)
 {
-    constexpr int NC = ROWLEN / 8;                 // 16-byte chunks per row
-    static_assert(NC == 4 || NC == 8 || NC == 16, "row length");
-    int f;
-    if constexpr (NC == 16) f = row & 15;
-    else if constexpr (NC == 8) f = (row & 7) ^ ((row >> 3) & 1);
-    else f = (row >> 2) & 3;
-    return row * ROWLEN + (((col >> 3) ^ f) << 3) + (col & 7);
+    static_assert(COLS % 32 == 0, "fragment columns");
+    return (((row >> 4) * (COLS / 32) + (col >> 5)) * 64 + (row & 15) + 16 * ((col >> 3) & 3)) * 8 + (col & 7);
 }
 
-// Element offset of (row r, col) in the compact Aqk layout (aq_width above):
-// tile t = r / 16 holds 16 rows of 32 (t < 2) or 64 (t >= 2) columns, each row
-// swizzled like swz.
-__device__ __forceinline__ int aq_index(int r, int col)
+// Element offset of (row r, col) in the compact Aqk tile (aq_width above):
+// token tile t = r / 16 keeps its aq_width(t) / 32 fragments, laid out as in
+// frag, after those of the tiles before it.
+__device__ __forceinline__ int aq_frag(int r, int col)
 {
     const int t = r >> 4;
-    const int w = t < 2 ? 32 : 64;
     const int base = t == 0 ? 0 : t == 1 ? 512 : t == 2 ? 1024 : 2048;
-    const int f = w == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
-    return base + (r & 15) * w + ((((col >> 3) ^ f) & (w / 8 - 1)) << 3) + (col & 7);
+    return base + ((col >> 5) * 64 + (r & 15) + 16 * ((col >> 3) & 3)) * 8 + (col & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -449,7 +442,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
             sKh[wave][kk][lane] = pack_bf16x8(kh);
             qt0[kk] = pack_bf16x8(qt);
             kt0[kk] = pack_bf16x8(kt);
-            *reinterpret_cast<bf16x8*>(wQ + swz<DKP>(r, c0)) = qt0[kk];
+            *reinterpret_cast<bf16x8*>(wQ + frag<DKP>(r, c0)) = qt0[kk];
             // Kb^T through the identity products: lane l gets channel
             // 32 kk + 16 half + l % 16, tokens 16 w + 4 (l / 16) .. + 3.
             const bf16x8 akb = pack_bf16x8(kb);
@@ -457,7 +450,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const f32x4 tb = mfma16x16x32(akb, half ? id1 : id0, zero);
-                *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(32 * kk + 16 * half + l16, 16 * wave + 4 * g4)) =
+                *reinterpret_cast<bf16x4*>(wKb + frag<BTP>(32 * kk + 16 * half + l16, 16 * wave + 4 * g4)) =
                     pack_bf16x4(tb);
             }
         }
@@ -465,7 +458,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     if (BTP > BT) {                           // token padding of Kb^T
         for (int idx = tid; idx < DKP * (BTP - BT) / 4; idx += kThreads) {
             const int c = idx / ((BTP - BT) / 4), s = BT + 4 * (idx % ((BTP - BT) / 4));
-            *reinterpret_cast<bf16x4*>(wKb + swz<BTP>(c, s)) = bf16x4{};
+            *reinterpret_cast<bf16x4*>(wKb + frag<BTP>(c, s)) = bf16x4{};
         }
     }
     __syncthreads();                          // sKh ready
@@ -516,10 +509,10 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                 aq[ii] = s <= r ? cq[ii] : 0.0f;
             }
             *reinterpret_cast<f32x4*>(&sM[r][16 * j + 4 * g4]) = mk;
-            *reinterpret_cast<bf16x4*>(wA + aq_index(r, 16 * j + 4 * g4)) = pack_bf16x4(aq);
+            *reinterpret_cast<bf16x4*>(wA + aq_frag(r, 16 * j + 4 * g4)) = pack_bf16x4(aq);
         }
         for (int j = wave + 1; j < P::aq_width(wave) / 16; ++j)   // above the diagonal
-            *reinterpret_cast<bf16x4*>(wA + aq_index(r, 16 * j + 4 * g4)) = bf16x4{};
+            *reinterpret_cast<bf16x4*>(wA + aq_frag(r, 16 * j + 4 * g4)) = bf16x4{};
         // T is zero above the diagonal blocks (and in the token padding).
         for (int cc = 16 * (wave + 1) + 4 * g4; cc < BTP; cc += 16)
             *reinterpret_cast<bf16x4*>(&sT[r][cc]) = bf16x4{};
@@ -617,7 +610,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                 if (kk <= kmax)
                     acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sKt[16 * mt + l16][32 * kk + 8 * g4]),
                                        tf[kk], acc);
-            *reinterpret_cast<bf16x4*>(wW + swz<DKP>(r, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
+            *reinterpret_cast<bf16x4*>(wW + frag<DKP>(r, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
         }
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) {
@@ -627,93 +620,78 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                 if (kk <= kmax)
                     acc = mfma16x16x32(tf[kk],
                                        *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][32 * kk + 8 * g4]), acc);
-            *reinterpret_cast<bf16x4*>(wU + swz<BTP>(16 * nt + l16, 16 * wave + 4 * g4)) = pack_bf16x4(acc);
+            *reinterpret_cast<bf16x4*>(wU + frag<BTP>(16 * nt + l16, 16 * wave + 4 * g4)) = pack_bf16x4(acc);
         }
     }
     if (BTP > BT)
         for (int idx = tid; idx < D * (BTP - BT) / 4; idx += kThreads) {
             const int row = idx / ((BTP - BT) / 4), c4 = idx % ((BTP - BT) / 4);
-            *reinterpret_cast<bf16x4*>(wU + swz<BTP>(row, BT + 4 * c4)) = bf16x4{};
+            *reinterpret_cast<bf16x4*>(wU + frag<BTP>(row, BT + 4 * c4)) = bf16x4{};
         }
 }
 
 // ---------------------------------------------------------------------------
 // chain_kernel: the state-dependent part, serial over a sequence's chunks.
 //
-// One workgroup per (sequence, head, 16-column d_v tile) with twelve waves
-// in three roles.  Each role runs its own loop over the chunks and every role
-// executes the same two barriers per chunk.  Phase 1 (before B1) reads S;
-// phase 2 (between B1 and B2) reads D and writes the next S:
+// One workgroup per (sequence, head, 16-column d_v tile) with eight waves in
+// two roles.  Every wave runs the same two barriers per chunk.  Phase 1
+// (before B1) reads S; phase 2 (between B1 and B2) reads D and writes the
+// next S:
 //   state waves 0-3    phase 1: D = U - W S for token tile w.
 //                      phase 2: S <- e^{G_C} S + Kb^T D for key tiles w, w+4.
 //                      S stays in fp32 accumulators and is shared as bf16 S^T.
 //   output waves 4-7   phase 1: Q~ S;  phase 2: + Aqk D, scaled and stored,
 //                      for token tile w-4 (computed transposed, so each lane
 //                      stores 4 consecutive columns of one output row).
-//   loader waves 8-11  stream the record into two LDS rings with
-//                      asynchronous global->LDS copies: ring A (W, Q~, the U
-//                      tile; read in phase 1) with 2 stages and ring B (Kb^T,
-//                      Aqk, e^{G_C}; read in phase 2) with 3 stages.  A stage
-//                      is refilled as soon as the phase that reads it has
-//                      passed its barrier, in two halves spread over the two
-//                      phases.
-// The copies share the CU's path from L2 into LDS (about 64 bytes per clock,
-// which also bounds LDS writes); with ~57 KB per chunk it bounds the time per
-// chunk together with the two dependent phases.  The eight tiles of one
+// Every byte of a chunk's record is an MFMA operand of exactly one wave (its
+// token tile of W, Q~ and Aqk, its key tiles of Kb^T, its slice of U), so
+// each wave loads its own operands from the record straight into registers,
+// kChainBufs - 1 chunks ahead of their use, and LDS carries only the bf16
+// S^T and D^T exchanged between the two roles.  The eight tiles of one
 // (sequence, head) are placed on one XCD by the grid order, so each record
 // comes from HBM into that XCD's L2 once.
-// Compute waves issue no global loads, and each loader wave owns one stream,
-// so no wave waits on another's prefetch (waits count per wave, in order).
-// The record's bf16 tiles are stored with swizzled 16-byte chunks (swz,
-// aq_index), so the linear copies land in LDS in a layout that 16 lanes
-// reading one chunk column of 16 rows read without bank conflicts.
-constexpr int kChainWaves = 12;
+constexpr int kChainWaves = 8;
 constexpr int kChainThreads = kChainWaves * kWave;
-constexpr int kStagesA = 2;
-constexpr int kStagesB = 3;
+constexpr int kChainBufs = 3;                      // register ring depth (chunks)
 
-constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
-constexpr int copy_ops(int bytes) { return (bytes + kWave * 16 - 1) / (kWave * 16); }
-
-template <int D, int BT>
-struct ChainRings {
-    using P = Shape<D, BT>;
-    // ring A stage
-    static constexpr int W_OFF = 0;                                   // W    [BT][DKP]
-    static constexpr int Q_OFF = W_OFF + BT * P::DKP * 2;             // Q~   [BT][DKP]
-    static constexpr int U_OFF = Q_OFF + BT * P::DKP * 2;             // U^T tile [16][BTP]
-    static constexpr int A_BYTES = round_up(U_OFF + 16 * P::BTP * 2, 512);
-    // ring B stage
-    static constexpr int KB_OFF = 0;                                  // Kb^T [DKP][BTP]
-    static constexpr int AQ_OFF = KB_OFF + P::DKP * P::BTP * 2;       // Aqk, compact
-    static constexpr int EG_OFF = AQ_OFF + P::AQ_ELEMS * 2;           // e^{G_C} [DKP] fp32
-    static constexpr int B_BYTES = round_up(EG_OFF + P::DKP * 4, 512);
-    // asynchronous copies (1 KB each) per stage and loader wave
-    static constexpr int OPS_L0 = copy_ops(BT * P::DKP * 2) + copy_ops(16 * P::BTP * 2);  // W, U
-    static constexpr int OPS_L1 = copy_ops(BT * P::DKP * 2);                              // Q~
-    static constexpr int OPS_L2 = copy_ops(P::DKP * P::BTP * 2);                          // Kb^T
-    static constexpr int OPS_L3 = copy_ops(P::AQ_ELEMS * 2) + copy_ops(P::DKP * 4);       // Aqk, e^G
-    // the first of the two halves each loader issues per chunk
-    static constexpr int OPS_L0_H0 = copy_ops(BT * P::DKP);                               // W, first half
-    static constexpr int OPS_L1_H0 = copy_ops(BT * P::DKP);                               // Q~, first half
-    static constexpr int OPS_L2_H0 = copy_ops(P::DKP * P::BTP);                           // Kb^T, first half
-    static constexpr int OPS_L3_H0 = copy_ops(P::AQ_ELEMS * 2);                           // Aqk
-    static_assert(OPS_L0 + OPS_L0_H0 < 64 && OPS_L1 + OPS_L1_H0 < 64, "vmcnt range");
-    static_assert(2 * OPS_L2 + OPS_L2_H0 < 64 && 2 * OPS_L3 + OPS_L3_H0 < 64, "vmcnt range");
-    static_assert(kStagesA * OPS_L0 < 64 && kStagesA * OPS_L1 < 64, "vmcnt range");
-    static_assert(kStagesB * OPS_L2 < 64 && kStagesB * OPS_L3 < 64, "vmcnt range");
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Copy `bytes` (a multiple of 16) from global `src` to LDS `dst` in 1-KB
-// asynchronous pieces; every piece is issued (lanes past the end idle), so the
-// number of memory operations is copy_ops(bytes).
-__device__ __forceinline__ void copy_async(uint8_t* dst, const uint8_t* src, int bytes, int lane)
+// Marks every register of `x` as read here, so that the loads that wrote it
+// are waited for at this point (and not later, behind a branch).
+template <typename T>
+__device__ __forceinline__ void consume(const T& x)
 {
-    for (int off = 0; off < bytes; off += kWave * 16) {
-        if (off + lane * 16 < bytes)
-            __builtin_amdgcn_global_load_lds((const void*)(src + off + lane * 16), (lds_void*)(dst + off), 16, 0, 0);
+    constexpr int N = sizeof(T) / 16;
+    static_assert(sizeof(T) % 16 == 0, "16-byte pieces");
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(&x);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        uint32_t a = p[4 * i], b = p[4 * i + 1], c = p[4 * i + 2], d = p[4 * i + 3];
+        asm volatile("" : : "v"(a), "v"(b), "v"(c), "v"(d));
+    }
+}
+
+// The chunk loop of one wave with a register ring of NB chunks: step lc
+// first starts the loads of chunk lc + NB - 1 into the buffer that step
+// lc - 1 used, then runs on the buffer of chunk lc.  The loop runs whole
+// groups of NB steps (so every buffer is used at a fixed place in the body)
+// and the last nch % NB steps after it.
+template <int NB, typename Ops, typename Fetch, typename Step>
+__device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, Step step)
+{
+    int c0 = 0;
+    for (; c0 + NB <= nch; c0 += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB]);
+            consume(buf[u]);
+            step(c0 + u, buf[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) {
+        if (c0 + u < nch) {
+            consume(buf[u]);
+            step(c0 + u, buf[u]);
+        }
     }
 }
 
@@ -726,13 +704,10 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                   const uint8_t* __restrict__ ws)
 {
     using P = Shape<D, BT>;
-    using R = ChainRings<D, BT>;
-    constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS;
+    constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NB = kChainBufs;
     constexpr int NKT_W = (P::NMT_K + 3) / 4;     // key m-tiles per state wave
     constexpr int SP = DKP + 8, DP = BTP + 8;     // bf16 pitches of the exchange tiles
 
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[kStagesA][R::A_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStagesB][R::B_BYTES];
     __shared__ __attribute__((aligned(16))) bf16 sS[16][SP];      // bf16 S^T of the tile
     __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // bf16 D^T
 
@@ -762,14 +737,18 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
     int64_t ckpt_base = 0;
     sequence_bases(cu, seq, BT, interval, lane, chunk_base, ckpt_base);
     const int nch = num_chunks(len, BT);
+    // Chunks past the last are clamped to it, so prefetches stay in bounds.
     auto record = [&](int lc) {
-        return ws + ((int64_t)(chunk_base + min(lc, nch - 1)) * heads + h) * P::REC_BYTES;
+        return reinterpret_cast<const bf16*>(
+            ws + ((int64_t)(chunk_base + min(lc, nch - 1)) * heads + h) * P::REC_BYTES);
     };
 
     if (wave < 4) {
         // ---------------- state waves ----------------
         const bool init = has_init ? has_init[seq] != 0 : true;
         ST* home = pool + ((int64_t)slot * heads + h) * (int64_t)(D * D);
+        const bool dwave = wave < NS;              // owns a token tile of D
+        const int tt = dwave ? wave : 0;
         float S[NKT_W][4];
 #pragma unroll
         for (int j = 0; j < NKT_W; ++j) {
@@ -788,51 +767,62 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
         }
         if (BTP > BT && wave == 0)                 // token padding of D^T stays zero
             *reinterpret_cast<bf16x4*>(&sD[l16][BT + 4 * g4]) = bf16x4{};
-        lds_barrier();                             // B0: S_0 published
 
-        for (int lc = 0; lc < nch; ++lc) {
-            const uint8_t* stA = sA[lc % kStagesA];
-            const uint8_t* stB = sB[lc % kStagesB];
-            const bf16* sW = reinterpret_cast<const bf16*>(stA + R::W_OFF);
-            const bf16* sU = reinterpret_cast<const bf16*>(stA + R::U_OFF);
-            const bf16* sKb = reinterpret_cast<const bf16*>(stB + R::KB_OFF);
-            const float* sEg = reinterpret_cast<const float*>(stB + R::EG_OFF);
-            if (wave < NS) {                       // D = U - W S, token tile `wave`
+        // This wave's operands of one chunk.
+        struct Ops {
+            bf16x8 w[P::NKK_K];                    // W rows of token tile tt
+            bf16x4 u;                              // U^T: column col, 4 tokens of tile tt
+            bf16x8 kb[NKT_W][P::NKK_T];            // Kb^T rows of key tiles wave + 4 j
+            f32x4 eg[NKT_W];                       // e^{G_C} of those rows
+        };
+        auto fetch = [&](int lc, Ops& o) {
+            const bf16* rec = record(lc);
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_K; ++kk)
+                o.w[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_W + frag<DKP>(16 * tt + l16, 32 * kk + 8 * g4));
+            o.u = *reinterpret_cast<const bf16x4*>(rec + P::OFF_U + frag<BTP>(col, 16 * tt + 4 * g4));
+#pragma unroll
+            for (int j = 0; j < NKT_W; ++j) {
+                const int kt = min(wave + 4 * j, P::NMT_K - 1);
+#pragma unroll
+                for (int kk = 0; kk < P::NKK_T; ++kk)
+                    o.kb[j][kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_KB + frag<BTP>(16 * kt + l16, 32 * kk + 8 * g4));
+                o.eg[j] = *reinterpret_cast<const f32x4*>(
+                    reinterpret_cast<const uint8_t*>(rec) + P::EG_BYTE_OFF + (16 * kt + 4 * g4) * 4);
+            }
+        };
+        auto step = [&](int lc, const Ops& o) {
+            if (dwave) {                           // D = U - W S, token tile tt
                 f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-                const int r = 16 * wave + l16;
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_K; ++kk) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sW + swz<DKP>(r, 32 * kk + 8 * g4));
                     const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
-                    if (kk & 1) acc1 = mfma16x16x32(a, b, acc1);
-                    else acc0 = mfma16x16x32(a, b, acc0);
+                    if (kk & 1) acc1 = mfma16x16x32(o.w[kk], b, acc1);
+                    else acc0 = mfma16x16x32(o.w[kk], b, acc0);
                 }
-                const bf16x4 u4 = *reinterpret_cast<const bf16x4*>(sU + swz<BTP>(l16, 16 * wave + 4 * g4));
                 bf16x4 d4;
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)
-                    d4[ii] = static_cast<bf16>(static_cast<float>(u4[ii]) - (acc0[ii] + acc1[ii]));
-                *reinterpret_cast<bf16x4*>(&sD[l16][16 * wave + 4 * g4]) = d4;
+                    d4[ii] = static_cast<bf16>(static_cast<float>(o.u[ii]) - (acc0[ii] + acc1[ii]));
+                *reinterpret_cast<bf16x4*>(&sD[l16][16 * tt + 4 * g4]) = d4;
             }
             lds_barrier();                         // B1
 #pragma unroll
             for (int j = 0; j < NKT_W; ++j) {      // S <- Diag(e^{G_C}) S + Kb^T D
                 const int kt = wave + 4 * j;
                 if (kt >= P::NMT_K) continue;
-                const f32x4 eg = *reinterpret_cast<const f32x4*>(sEg + 16 * kt + 4 * g4);
                 f32x4 acc;
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) acc[ii] = S[j][ii] * eg[ii];
+                for (int ii = 0; ii < 4; ++ii) acc[ii] = S[j][ii] * o.eg[j][ii];
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_T; ++kk)
-                    acc = mfma16x16x32(
-                        *reinterpret_cast<const bf16x8*>(sKb + swz<BTP>(16 * kt + l16, 32 * kk + 8 * g4)),
-                        *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) S[j][ii] = acc[ii];
+                    acc = mfma16x16x32(o.kb[j][kk], *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc);
                 bf16x4 s4;
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) s4[ii] = static_cast<bf16>(S[j][ii]);
+                for (int ii = 0; ii < 4; ++ii) {
+                    S[j][ii] = acc[ii];
+                    s4[ii] = static_cast<bf16>(acc[ii]);
+                }
                 *reinterpret_cast<bf16x4*>(&sS[l16][16 * kt + 4 * g4]) = s4;
             }
             const int pos = (lc + 1) * BT;         // checkpoint at this chunk's end
@@ -852,7 +842,12 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 }
             }
             lds_barrier();                         // B2
-        }
+        };
+        Ops buf[NB];
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
+        lds_barrier();                             // B0: S_0 published
+        run_steps<NB>(nch, buf, fetch, step);
 #pragma unroll
         for (int j = 0; j < NKT_W; ++j) {          // final state, in place
             const int kt = wave + 4 * j;
@@ -862,27 +857,36 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 if (kt < P::NMT_K && rr < D) home[(int64_t)rr * D + col] = from_f32<ST>(S[j][ii]);
             }
         }
-    } else if (wave < 8) {
+    } else {
         // ---------------- output waves ----------------
         // O^T = S^T Q~^T + D^T Aqk^T: with the operands of O = Q~ S + Aqk D
         // swapped, lane l holds 4 consecutive columns of output row
         // 16 tt + l % 16 and writes them with one vector store.
-        const int tt = wave - 4;                   // token tile
-        const bool active = tt < NS;
+        const bool active = wave - 4 < NS;
+        const int tt = active ? wave - 4 : 0;      // token tile
         const int kmax = (16 * tt + 15) / 32;      // Aqk is zero beyond the diagonal
-        const int r = 16 * (active ? tt : 0) + l16;
-        lds_barrier();                             // B0
-        for (int lc = 0; lc < nch; ++lc) {
-            const bf16* sQ = reinterpret_cast<const bf16*>(sA[lc % kStagesA] + R::Q_OFF);
-            const bf16* sAq = reinterpret_cast<const bf16*>(sB[lc % kStagesB] + R::AQ_OFF);
+        const int r = 16 * tt + l16;
+        struct Ops {
+            bf16x8 q[P::NKK_K];                    // Q~ rows of token tile tt
+            bf16x8 a[P::NKK_T];                    // Aqk rows of token tile tt
+        };
+        auto fetch = [&](int lc, Ops& o) {
+            const bf16* rec = record(lc);
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_K; ++kk)
+                o.q[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_Q + frag<DKP>(r, 32 * kk + 8 * g4));
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_T; ++kk)
+                o.a[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_A + aq_frag(r, 32 * min(kk, kmax) + 8 * g4));
+        };
+        auto step = [&](int lc, const Ops& o) {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
             if (active) {
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_K; ++kk) {
                     const bf16x8 sf = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
-                    const bf16x8 qf = *reinterpret_cast<const bf16x8*>(sQ + swz<DKP>(r, 32 * kk + 8 * g4));
-                    if (kk & 1) acc1 = mfma16x16x32(sf, qf, acc1);
-                    else acc0 = mfma16x16x32(sf, qf, acc0);
+                    if (kk & 1) acc1 = mfma16x16x32(sf, o.q[kk], acc1);
+                    else acc0 = mfma16x16x32(sf, o.q[kk], acc0);
                 }
             }
             lds_barrier();                         // B1
@@ -890,9 +894,7 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_T; ++kk)
                     if (kk <= kmax)
-                        acc0 = mfma16x16x32(
-                            *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]),
-                            *reinterpret_cast<const bf16x8*>(sAq + aq_index(r, 32 * kk + 8 * g4)), acc0);
+                        acc0 = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), o.a[kk], acc0);
                 const int64_t tc = s_begin + (int64_t)lc * BT;
                 if (r < min(BT, len - lc * BT)) {
                     float o4[4];
@@ -902,71 +904,12 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 }
             }
             lds_barrier();                         // B2
-        }
-    } else if (wave < 10) {
-        // ---------------- ring A loaders ----------------
-        // Stage lc % 2 is read in phase 1 of chunk lc.  Chunk lc + 2 goes
-        // into it in two halves, after B1 and after B2 of chunk lc, so that
-        // the copies are spread over both phases; chunk lc + 1 must be
-        // complete by B2 of chunk lc.
-        const int lw = wave - 8;
-        auto issue = [&](int lc, int part) {
-            uint8_t* dst = sA[lc % kStagesA];
-            const uint8_t* rec = record(lc);
-            constexpr int HALF = BT * DKP;          // bytes: half of W or of Q~
-            if (lw == 0) {
-                copy_async(dst + R::W_OFF + part * HALF, rec + P::OFF_W * 2 + part * HALF, HALF, lane);
-                if (part)
-                    copy_async(dst + R::U_OFF, rec + (P::OFF_U + (int64_t)n0 * BTP) * 2, 16 * BTP * 2, lane);
-            } else {
-                copy_async(dst + R::Q_OFF + part * HALF, rec + P::OFF_Q * 2 + part * HALF, HALF, lane);
-            }
         };
-        issue(0, 0); issue(0, 1);
-        issue(1, 0); issue(1, 1);
-        if (lw == 0) wait_vmcnt<R::OPS_L0>();      // chunk 0 complete
-        else wait_vmcnt<R::OPS_L1>();
+        Ops buf[NB];
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
         lds_barrier();                             // B0
-        for (int lc = 0; lc < nch; ++lc) {
-            lds_barrier();                         // B1
-            issue(lc + 2, 0);
-            if (lw == 0) wait_vmcnt<R::OPS_L0_H0>();   // chunk lc + 1 complete
-            else wait_vmcnt<R::OPS_L1_H0>();
-            lds_barrier();                         // B2
-            issue(lc + 2, 1);
-        }
-        wait_vmcnt<0>();
-    } else {
-        // ---------------- ring B loaders ----------------
-        // Stage lc % 3 is read in phase 2 of chunk lc.  Chunk lc + 3 goes
-        // into it in two halves, after B2 of chunk lc and after B1 of chunk
-        // lc + 1; chunk lc must be complete by B1 of chunk lc.
-        const int lw = wave - 10;
-        auto issue = [&](int lc, int part) {
-            uint8_t* dst = sB[lc % kStagesB];
-            const uint8_t* rec = record(lc);
-            if (lw == 0) {
-                constexpr int HALF = DKP * BTP;     // bytes: half of Kb^T
-                copy_async(dst + R::KB_OFF + part * HALF, rec + P::OFF_KB * 2 + part * HALF, HALF, lane);
-            } else if (part == 0) {
-                copy_async(dst + R::AQ_OFF, rec + P::OFF_A * 2, P::AQ_ELEMS * 2, lane);
-            } else {
-                copy_async(dst + R::EG_OFF, rec + P::EG_BYTE_OFF, DKP * 4, lane);
-            }
-        };
-        issue(0, 0); issue(0, 1);
-        issue(1, 0); issue(1, 1);
-        issue(2, 0);
-        lds_barrier();                             // B0
-        for (int lc = 0; lc < nch; ++lc) {
-            if (lw == 0) wait_vmcnt<R::OPS_L2 + R::OPS_L2_H0>();   // chunk lc complete
-            else wait_vmcnt<R::OPS_L3 + R::OPS_L3_H0>();
-            lds_barrier();                         // B1
-            issue(lc + 2, 1);
-            lds_barrier();                         // B2
-            issue(lc + 3, 0);
-        }
-        wait_vmcnt<0>();
+        run_steps<NB>(nch, buf, fetch, step);
     }
 }
 
