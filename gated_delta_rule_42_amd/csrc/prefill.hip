@@ -39,6 +39,8 @@
 // Off-diagonal blocks have both factors <= 1; diagonal blocks grow at most by
 // the decay accumulated inside one sub-chunk, which must stay above e^{-80}.
 
+#include <type_traits>
+
 #include "kda_device.cuh"
 #include "kda_internal.h"
 
@@ -260,7 +262,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                   int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ g,
                   const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
                   int heads, const int32_t* __restrict__ slots, uint32_t flags,
-                  uint8_t* __restrict__ ws)
+                  uint8_t* __restrict__ ws, int64_t flag_off, int64_t n_flags)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NKK = P::NKK_K;
@@ -298,6 +300,11 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, g4 = lane >> 4;
 
+    if (wave == 0) {                         // the chain kernel's flags start at zero
+        uint32_t* fl = reinterpret_cast<uint32_t*>(ws + flag_off);
+        const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+        for (int64_t i = ((int64_t)h * gridDim.x + x) * kWave + lane; i < n_flags; i += nwg * kWave) fl[i] = 0;
+    }
     int seq = 0, first = 0;
     if (!locate_chunk(cu, n_seqs, BT, x, lane, seq, first)) return;
     if (slots[seq] < 0) return;              // padding sequence: nothing to precompute
@@ -633,26 +640,47 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
 // ---------------------------------------------------------------------------
 // chain_kernel: the state-dependent part, serial over a sequence's chunks.
 //
-// One workgroup per (sequence, head, 16-column d_v tile) with eight waves in
-// two roles.  Every wave runs the same two barriers per chunk.  Phase 1
-// (before B1) reads S; phase 2 (between B1 and B2) reads D and writes the
-// next S:
-//   state waves 0-3    phase 1: D = U - W S for token tile w.
-//                      phase 2: S <- e^{G_C} S + Kb^T D for key tiles w, w+4.
-//                      S stays in fp32 accumulators and is shared as bf16 S^T.
-//   output waves 4-7   phase 1: Q~ S;  phase 2: + Aqk D, scaled and stored,
-//                      for token tile w-4 (computed transposed, so each lane
-//                      stores 4 consecutive columns of one output row).
-// Every byte of a chunk's record is an MFMA operand of exactly one wave (its
-// token tile of W, Q~ and Aqk, its key tiles of Kb^T, its slice of U), so
-// each wave loads its own operands from the record straight into registers,
-// kChainBufs - 1 chunks ahead of their use, and LDS carries only the bf16
-// S^T and D^T exchanged between the two roles.  The eight tiles of one
-// (sequence, head) are placed on one XCD by the grid order, so each record
-// comes from HBM into that XCD's L2 once.
-constexpr int kChainWaves = 8;
+// Two workgroups per (sequence, head, 16-column d_v tile), on two CUs of one
+// XCD:
+//   state workgroup    4 waves, two barriers per chunk.  Phase 1: wave w
+//   (blockIdx.z = 0)   computes D = U - W S for token tile w; phase 2:
+//                      S <- e^{G_C} S + Kb^T D for key tiles w, w + 4.  S stays
+//                      in fp32 accumulators and is shared as bf16 through LDS.
+//                      Each chunk's S (at its start) and D go, in bf16, to the
+//                      chunk's exchange slot in the workspace; once they have
+//                      landed in L2 the chunk count is published in a flag.
+//   output workgroup   4 output waves and a loader wave, one barrier per
+//   (blockIdx.z = 1)   chunk.  The loader waits for the flag and copies the
+//                      chunk's S and D from its slot into LDS, two chunks
+//                      ahead; output wave t writes O = scale (Q~ S + Aqk D)
+//                      for token tile t, computed transposed so each lane
+//                      stores 4 consecutive columns.
+// Every byte of a record is an MFMA operand of exactly one wave, so each
+// compute wave loads its own record operands straight into a register ring
+// kChainBufs - 1 chunks ahead.  Splitting the roles halves what one CU pulls
+// from L2 per chunk, which is what bounds the chain (W, Kb^T, U, e^{G_C} on
+// one CU; Q~, Aqk and the 6 KB of S and D on the other).
+//
+// The exchange goes through the XCD's L2: plain stores, and loads that skip
+// the CU's L1.  Workgroups are dealt to the XCDs round-robin by linear id and
+// the two roles of a tile are 8 * k ids apart, so they share an XCD.  The
+// flag carries the state workgroup's XCD id and the output workgroup checks
+// it; if the two ever ran on different XCDs the output workgroup would never
+// see the flag move and writes NaN after a bounded wait instead of stale
+// results.  State workgroups come first in the grid, so every output
+// workgroup's producer is already running when it starts waiting.
+constexpr int kChainWaves = 5;
 constexpr int kChainThreads = kChainWaves * kWave;
 constexpr int kChainBufs = 3;                      // register ring depth (chunks)
+constexpr int kXchStages = 3;                      // LDS stages of S and D (output workgroup)
+// Spin limit of the output workgroup's loader waiting for a chunk; the state
+// workgroup publishes one every microsecond or so, so this is a safety net.
+constexpr int kMaxSpin = 1 << 20;
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+constexpr int kBufferRsrcWord3 = 0x00020000;       // raw 32-bit buffer descriptor
+constexpr int kSkipL1 = 1;                         // cache policy: coherent in the XCD's L2 (sc0)
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Marks every register of `x` as read here, so that the loads that wrote it
 // are waited for at this point (and not later, behind a branch).
@@ -669,11 +697,11 @@ __device__ __forceinline__ void consume(const T& x)
     }
 }
 
-// The chunk loop of one wave with a register ring of NB chunks: step lc
-// first starts the loads of chunk lc + NB - 1 into the buffer that step
-// lc - 1 used, then runs on the buffer of chunk lc.  The loop runs whole
-// groups of NB steps (so every buffer is used at a fixed place in the body)
-// and the last nch % NB steps after it.
+// The chunk loop of one wave with a register ring of NB chunks.  The loop
+// runs whole groups of NB steps (so every buffer is used at a fixed place in
+// the body) and the last nch % NB steps after it.  Step lc runs on the buffer
+// of chunk lc and calls `refill` once, which starts the loads of chunk
+// lc + NB - 1 into the buffer that step lc - 1 used.
 template <int NB, typename Ops, typename Fetch, typename Step>
 __device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, Step step)
 {
@@ -681,16 +709,15 @@ __device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, 
     for (; c0 + NB <= nch; c0 += NB) {
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB]);
             consume(buf[u]);
-            step(c0 + u, buf[u]);
+            step(c0 + u, buf[u], [&]() { fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB]); });
         }
     }
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u) {
         if (c0 + u < nch) {
             consume(buf[u]);
-            step(c0 + u, buf[u]);
+            step(c0 + u, buf[u], [&]() { fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB]); });
         }
     }
 }
@@ -701,34 +728,41 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                   ST* __restrict__ pool, int64_t num_slots, const int32_t* __restrict__ slots,
                   const uint8_t* __restrict__ has_init, ST* __restrict__ ckpt, int64_t ckpt_cap,
                   int interval, float scale, AT* __restrict__ out, int64_t os,
-                  const uint8_t* __restrict__ ws)
+                  uint8_t* __restrict__ ws, int64_t xch_off, int64_t xch_chunks, int64_t flag_off)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NB = kChainBufs;
     constexpr int NKT_W = (P::NMT_K + 3) / 4;     // key m-tiles per state wave
-    constexpr int SP = DKP + 8, DP = BTP + 8;     // bf16 pitches of the exchange tiles
+    constexpr int SP = DKP + 8, DP = BTP + 8;     // bf16 pitches of the LDS tiles
+    // Exchange slot of one chunk: S^T [16][DKP] then D^T [16][BTP], bf16, in
+    // operand-fragment order.
+    constexpr int XS_BYTES = 16 * DKP * 2, XSLOT = XS_BYTES + 16 * BTP * 2;
+    static_assert(XSLOT % (kWave * 16) == 0, "exchange slot in 1 KB pieces");
 
-    __shared__ __attribute__((aligned(16))) bf16 sS[16][SP];      // bf16 S^T of the tile
-    __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // bf16 D^T
+    __shared__ __attribute__((aligned(16))) bf16 sS[16][SP];      // state: bf16 S^T of the tile
+    __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // state: bf16 D^T
+    __shared__ __attribute__((aligned(1024))) uint8_t sX[kXchStages][XSLOT];   // output: S, D
 
     // blockIdx.x enumerates (sequence, head) pairs, padded to a multiple of 8,
-    // and blockIdx.y the column tile: workgroups are dealt to the 8 XCDs
-    // round-robin by linear id, so all tiles of one pair share an XCD and its L2.
+    // blockIdx.y the column tile and blockIdx.z the role.
     const int pair = blockIdx.x;
     if (pair >= n_seqs * heads) return;
     const int seq = pair / heads, h = pair % heads, tile = blockIdx.y, n0 = tile * 16;
+    const bool state_role = blockIdx.z == 0;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     __builtin_assume(wave >= 0 && wave < kChainWaves);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int col = n0 + l16;
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 15;   // HW_REG_XCC_ID
 
     const int64_t s_begin = cu[seq];
     const int len = max(0, cu[seq + 1] - cu[seq]);
     const int slot = slots[seq];
     if (slot < 0) {                                // graph padding: zero output rows
-        for (int idx = tid; idx < len * 16; idx += kChainThreads)
-            out[(s_begin + idx / 16) * os + (int64_t)h * D + n0 + idx % 16] = from_f32<AT>(0.0f);
+        if (!state_role)
+            for (int idx = tid; idx < len * 16; idx += kChainThreads)
+                out[(s_begin + idx / 16) * os + (int64_t)h * D + n0 + idx % 16] = from_f32<AT>(0.0f);
         return;
     }
     if (len == 0 || slot >= num_slots) return;
@@ -742,9 +776,12 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
         return reinterpret_cast<const bf16*>(
             ws + ((int64_t)(chunk_base + min(lc, nch - 1)) * heads + h) * P::REC_BYTES);
     };
+    uint8_t* const xch = ws + xch_off + ((int64_t)(h * (D / 16) + tile) * xch_chunks + chunk_base) * XSLOT;
+    uint32_t* const flag = reinterpret_cast<uint32_t*>(ws + flag_off) + ((int64_t)seq * heads + h) * (D / 16) + tile;
 
-    if (wave < 4) {
-        // ---------------- state waves ----------------
+    if (state_role) {
+        // ---------------- state workgroup ----------------
+        if (wave >= 4) return;
         const bool init = has_init ? has_init[seq] != 0 : true;
         ST* home = pool + ((int64_t)slot * heads + h) * (int64_t)(D * D);
         const bool dwave = wave < NS;              // owns a token tile of D
@@ -768,13 +805,13 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
         if (BTP > BT && wave == 0)                 // token padding of D^T stays zero
             *reinterpret_cast<bf16x4*>(&sD[l16][BT + 4 * g4]) = bf16x4{};
 
-        // This wave's operands of one chunk.
         struct Ops {
             bf16x8 w[P::NKK_K];                    // W rows of token tile tt
             bf16x4 u;                              // U^T: column col, 4 tokens of tile tt
             bf16x8 kb[NKT_W][P::NKK_T];            // Kb^T rows of key tiles wave + 4 j
             f32x4 eg[NKT_W];                       // e^{G_C} of those rows
         };
+        constexpr int LOADS = P::NKK_K + 1 + NKT_W * (P::NKK_T + 1);   // loads per fetch
         auto fetch = [&](int lc, Ops& o) {
             const bf16* rec = record(lc);
 #pragma unroll
@@ -791,7 +828,18 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                     reinterpret_cast<const uint8_t*>(rec) + P::EG_BYTE_OFF + (16 * kt + 4 * g4) * 4);
             }
         };
-        auto step = [&](int lc, const Ops& o) {
+        auto step = [&](int lc, const Ops& o, auto refill) {
+            uint8_t* const slot_x = xch + (int64_t)lc * XSLOT;
+            // This chunk's S (its start state) to the exchange slot.
+#pragma unroll
+            for (int j = 0; j < NKT_W; ++j) {
+                const int kt = wave + 4 * j;
+                if (kt >= P::NMT_K) continue;
+                bf16x4 s4;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) s4[ii] = static_cast<bf16>(S[j][ii]);
+                *reinterpret_cast<bf16x4*>(slot_x + 2 * frag<DKP>(l16, 16 * kt + 4 * g4)) = s4;
+            }
             if (dwave) {                           // D = U - W S, token tile tt
                 f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -805,7 +853,12 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 for (int ii = 0; ii < 4; ++ii)
                     d4[ii] = static_cast<bf16>(static_cast<float>(o.u[ii]) - (acc0[ii] + acc1[ii]));
                 *reinterpret_cast<bf16x4*>(&sD[l16][16 * tt + 4 * g4]) = d4;
+                *reinterpret_cast<bf16x4*>(slot_x + XS_BYTES + 2 * frag<BTP>(l16, 16 * tt + 4 * g4)) = d4;
             }
+            if (BTP > BT && wave == 0)             // token padding of D^T
+                *reinterpret_cast<bf16x4*>(slot_x + XS_BYTES + 2 * frag<BTP>(l16, BT + 4 * g4)) = bf16x4{};
+            asm volatile("" ::: "memory");         // the refill's loads come after the stores
+            refill();
             lds_barrier();                         // B1
 #pragma unroll
             for (int j = 0; j < NKT_W; ++j) {      // S <- Diag(e^{G_C}) S + Kb^T D
@@ -841,7 +894,15 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                     }
                 }
             }
+            // This step's exchange stores are older than the refill's LOADS
+            // loads, so they have reached L2 once at most LOADS (plus any newer
+            // checkpoint stores) remain outstanding.
+            asm volatile("" ::: "memory");
+            wait_vmcnt<LOADS>();
             lds_barrier();                         // B2
+            if (wave == 0 && lane == 0)
+                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)(lc + 1), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
         };
         Ops buf[NB];
 #pragma unroll
@@ -857,67 +918,132 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 if (kt < P::NMT_K && rr < D) home[(int64_t)rr * D + col] = from_f32<ST>(S[j][ii]);
             }
         }
-    } else {
-        // ---------------- output waves ----------------
-        // O^T = S^T Q~^T + D^T Aqk^T: with the operands of O = Q~ S + Aqk D
-        // swapped, lane l holds 4 consecutive columns of output row
-        // 16 tt + l % 16 and writes them with one vector store.
-        const bool active = wave - 4 < NS;
-        const int tt = active ? wave - 4 : 0;      // token tile
-        const int kmax = (16 * tt + 15) / 32;      // Aqk is zero beyond the diagonal
-        const int r = 16 * tt + l16;
-        struct Ops {
-            bf16x8 q[P::NKK_K];                    // Q~ rows of token tile tt
-            bf16x8 a[P::NKK_T];                    // Aqk rows of token tile tt
+        return;
+    }
+
+    // ---------------- output workgroup ----------------
+    __shared__ int sBroken;                        // the flag never came: write NaN
+    if (wave == 4) {
+        // Loader: chunk c's S and D land in stage c % kXchStages before the
+        // barrier that ends step c - 1 (the prologue's barrier for c = 0).
+        bool broken = false;
+        auto wait_chunk = [&](int c) {             // until chunk c is published
+            if (broken) return;
+            for (int spin = 0; spin < kMaxSpin; ++spin) {
+                // Polled with device-scope atomic loads: a plain load can keep
+                // hitting the CU's own cached copy of the flag.
+                const uint32_t f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((f >> 24) == xcc && (f & 0xffffff) > (uint32_t)c) return;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            broken = true;
         };
-        auto fetch = [&](int lc, Ops& o) {
-            const bf16* rec = record(lc);
+        auto copy = [&](int c) {                   // 1 KB pieces, device-coherent at L2
+            const uint8_t* src = xch + (int64_t)min(c, nch - 1) * XSLOT;
+            uint8_t* dst = sX[c % kXchStages];
 #pragma unroll
-            for (int kk = 0; kk < P::NKK_K; ++kk)
-                o.q[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_Q + frag<DKP>(r, 32 * kk + 8 * g4));
+            for (int off = 0; off < XSLOT; off += kWave * 16)
+                __builtin_amdgcn_global_load_lds((const void*)(src + off + lane * 16), (lds_void*)(dst + off), 16, 0,
+                                                 kSkipL1);
+        };
+        constexpr int OPS = XSLOT / (kWave * 16);
+        wait_chunk(0); copy(0);
+        wait_chunk(min(1, nch - 1)); copy(1);
+        wait_vmcnt<OPS>();                         // chunk 0 landed
+        if (lane == 0) sBroken = broken;
+        lds_barrier();                             // publishes chunk 0
+        for (int c = 0; c < nch; ++c) {
+            // Stage (c + 2) % 3 was read in step c - 1, which ended at the
+            // barrier above.
+            wait_chunk(min(c + 2, nch - 1));
+            copy(c + 2);
+            wait_vmcnt<OPS>();                     // chunk c + 1 landed
+            if (lane == 0 && broken) sBroken = 1;
+            lds_barrier();                         // end of step c
+        }
+        wait_vmcnt<0>();
+        return;
+    }
+    // Output waves.
+    // O^T = S^T Q~^T + D^T Aqk^T: with the operands of O = Q~ S + Aqk D
+    // swapped, lane l holds 4 consecutive columns of output row
+    // 16 tt + l % 16 and writes them with one vector store.
+    const bool active = wave < NS;
+    const int tt = active ? wave : 0;              // token tile
+    const int kmax = (16 * tt + 15) / 32;          // Aqk is zero beyond the diagonal
+    const int r = 16 * tt + l16;
+    struct Ops {
+        bf16x8 q[P::NKK_K];                        // Q~ rows of token tile tt
+        bf16x8 a[P::NKK_T];                        // Aqk rows of token tile tt
+    };
+    auto fetch = [&](int lc, Ops& o) {
+        const bf16* rec = record(lc);
+#pragma unroll
+        for (int kk = 0; kk < P::NKK_K; ++kk)
+            o.q[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_Q + frag<DKP>(r, 32 * kk + 8 * g4));
+#pragma unroll
+        for (int kk = 0; kk < P::NKK_T; ++kk)
+            o.a[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_A + aq_frag(r, 32 * min(kk, kmax) + 8 * g4));
+    };
+    auto step = [&](int lc, const Ops& o, auto refill) {
+        refill();
+        if (active) {
+            const uint8_t* x = sX[lc % kXchStages];
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_K; ++kk) {
+                const bf16x8 sf = *reinterpret_cast<const bf16x8*>(x + (kk * kWave + lane) * 16);
+                if (kk & 1) acc1 = mfma16x16x32(sf, o.q[kk], acc1);
+                else acc0 = mfma16x16x32(sf, o.q[kk], acc0);
+            }
 #pragma unroll
             for (int kk = 0; kk < P::NKK_T; ++kk)
-                o.a[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_A + aq_frag(r, 32 * min(kk, kmax) + 8 * g4));
-        };
-        auto step = [&](int lc, const Ops& o) {
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-            if (active) {
+                if (kk <= kmax)
+                    acc0 = mfma16x16x32(*reinterpret_cast<const bf16x8*>(x + XS_BYTES + (kk * kWave + lane) * 16),
+                                        o.a[kk], acc0);
+            const int64_t tc = s_begin + (int64_t)lc * BT;
+            if (r < min(BT, len - lc * BT)) {
+                const float bad = sBroken ? __builtin_nanf("") : 1.0f;
+                float o4[4];
 #pragma unroll
-                for (int kk = 0; kk < P::NKK_K; ++kk) {
-                    const bf16x8 sf = *reinterpret_cast<const bf16x8*>(&sS[l16][32 * kk + 8 * g4]);
-                    if (kk & 1) acc1 = mfma16x16x32(sf, o.q[kk], acc1);
-                    else acc0 = mfma16x16x32(sf, o.q[kk], acc0);
-                }
+                for (int ii = 0; ii < 4; ++ii) o4[ii] = bad * scale * (acc0[ii] + acc1[ii]);
+                store4(out + (tc + r) * os + (int64_t)h * D + n0 + 4 * g4, o4);
             }
-            lds_barrier();                         // B1
-            if (active) {
+        }
+        lds_barrier();                             // end of step lc
+    };
+    Ops buf[NB];
 #pragma unroll
-                for (int kk = 0; kk < P::NKK_T; ++kk)
-                    if (kk <= kmax)
-                        acc0 = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), o.a[kk], acc0);
-                const int64_t tc = s_begin + (int64_t)lc * BT;
-                if (r < min(BT, len - lc * BT)) {
-                    float o4[4];
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) o4[ii] = scale * (acc0[ii] + acc1[ii]);
-                    store4(out + (tc + r) * os + (int64_t)h * D + n0 + 4 * g4, o4);
-                }
-            }
-            lds_barrier();                         // B2
-        };
-        Ops buf[NB];
-#pragma unroll
-        for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
-        lds_barrier();                             // B0
-        run_steps<NB>(nch, buf, fetch, step);
-    }
+    for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
+    lds_barrier();                                 // chunk 0 of S and D in LDS
+    run_steps<NB>(nch, buf, fetch, step);
 }
 
 // ---------------------------------------------------------------------------
+// Workspace: the records, then the chain's exchange slots (per head and
+// column tile, one per chunk slot), then one flag per (sequence, head, tile).
+struct WorkspaceLayout {
+    int64_t chunks, xch_off, flag_off, n_flags, bytes;
+};
+template <int D, int BT>
+WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t total_tokens, int32_t heads)
+{
+    using P = Shape<D, BT>;
+    WorkspaceLayout l;
+    l.chunks = max_chunks(num_seqs, total_tokens, BT);
+    const int64_t xslot = 16 * (P::DKP + P::BTP) * 2;
+    l.xch_off = l.chunks * heads * P::REC_BYTES;
+    l.flag_off = l.xch_off + (int64_t)heads * (D / 16) * l.chunks * xslot;
+    l.n_flags = (int64_t)num_seqs * heads * (D / 16);
+    l.bytes = l.flag_off + (l.n_flags * 4 + 255) / 256 * 256;
+    return l;
+}
+
 template <int D, int BT, typename AT, typename ST>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 {
-    const int64_t chunks = max_chunks(a.num_seqs, a.total_tokens, BT);
+    const WorkspaceLayout lay = workspace_layout<D, BT>(a.num_seqs, a.total_tokens, a.heads);
+    const int64_t chunks = lay.chunks;
     if (chunks > INT32_MAX) return hipErrorInvalidValue;
     const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;
     if (pairs > INT32_MAX) return hipErrorInvalidValue;
@@ -930,7 +1056,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                            dim3(kThreads), 0, stream, static_cast<const AT*>(a.q),
                            static_cast<const AT*>(a.k), static_cast<const AT*>(a.v), a.q_stride,
                            a.k_stride, a.v_stride, a.g, a.beta, a.cu_seqlens, a.num_seqs, a.heads,
-                           a.slots, a.flags, static_cast<uint8_t*>(a.workspace));
+                           a.slots, a.flags, static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -938,12 +1064,12 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         const hipError_t e = hipEventRecord(a.ev[1], stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST>), dim3((unsigned)pairs, (unsigned)(D / 16)),
+    hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST>), dim3((unsigned)pairs, (unsigned)(D / 16), 2u),
                        dim3(kChainThreads), 0, stream, a.cu_seqlens, a.num_seqs, a.heads,
                        static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                        static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
-                       static_cast<AT*>(a.out), a.out_stride,
-                       static_cast<const uint8_t*>(a.workspace));
+                       static_cast<AT*>(a.out), a.out_stride, static_cast<uint8_t*>(a.workspace),
+                       lay.xch_off, lay.chunks, lay.flag_off);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.ev[2]) return e;
     return hipEventRecord(a.ev[2], stream);
@@ -970,36 +1096,28 @@ hipError_t launch_chunk(const PrefillArgs& a, hipStream_t stream)
     }
 }
 
-template <int D, int BT>
-int64_t record_bytes() { return Shape<D, BT>::REC_BYTES; }
-
-template <int D>
-int64_t record_bytes_chunk(int32_t chunk)
-{
-    switch (chunk) {
-        case 16: return record_bytes<D, 16>();
-        case 32: return record_bytes<D, 32>();
-        case 64: return record_bytes<D, 64>();
-        default: return 0;
-    }
-}
-
 }  // namespace
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t heads, int32_t dk,
                                int32_t dv, int32_t chunk)
 {
     if (dk != dv) return 0;
-    int64_t rec = 0;
+    auto by_chunk = [&](auto dtag) -> int64_t {
+        constexpr int D = decltype(dtag)::value;
+        switch (chunk) {
+            case 16: return workspace_layout<D, 16>(num_seqs, total_tokens, heads).bytes;
+            case 32: return workspace_layout<D, 32>(num_seqs, total_tokens, heads).bytes;
+            case 64: return workspace_layout<D, 64>(num_seqs, total_tokens, heads).bytes;
+            default: return 0;
+        }
+    };
     switch (dk) {
-        case 16: rec = record_bytes_chunk<16>(chunk); break;
-        case 32: rec = record_bytes_chunk<32>(chunk); break;
-        case 64: rec = record_bytes_chunk<64>(chunk); break;
-        case 128: rec = record_bytes_chunk<128>(chunk); break;
+        case 16: return (size_t)by_chunk(std::integral_constant<int, 16>{});
+        case 32: return (size_t)by_chunk(std::integral_constant<int, 32>{});
+        case 64: return (size_t)by_chunk(std::integral_constant<int, 64>{});
+        case 128: return (size_t)by_chunk(std::integral_constant<int, 128>{});
         default: return 0;
     }
-    if (rec == 0) return 0;
-    return (size_t)(max_chunks(num_seqs, total_tokens, chunk) * heads * rec);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)

@@ -128,7 +128,11 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *               sequence are left alone.
  *   workspace   at least kda_chunk_prefill_workspace_size(...) bytes, 256-byte
  *               aligned.  Its contents are scratch: any call may overwrite it,
- *               so concurrent calls need separate workspaces.
+ *               so concurrent calls need separate workspaces.  It also carries
+ *               the per-chunk exchange between the two workgroups that share
+ *               each 16-column tile of the state; should the GPU ever place
+ *               such a pair on different XCDs, that tile's output rows come out
+ *               NaN (never stale values).
  * States are computed in fp32 between chunks; a bf16 state is rounded to
  * nearest-even when stored (final state and checkpoints).
  */

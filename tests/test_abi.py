@@ -61,8 +61,13 @@ def test_workspace_size(lib):
     from gated_delta_rule_42_amd import kda
     one = kda.chunk_prefill_workspace_size(1, 64, 1, 128, 128, 64)
     assert one > 0 and one % 256 == 0
-    # One record per (chunk slot, head); chunk slots = ceil(T / C) + N.
-    assert kda.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64) == (64 + 1) * 16 * (one // 2)
+    # Per (chunk slot, head): one record and the chain's exchange slots (one per
+    # 16-column tile); chunk slots = ceil(T / C) + N.  Then one 32-bit flag per
+    # (sequence, head, tile), rounded up to 256 bytes.
+    flags = lambda n, h: (n * h * (128 // 16) * 4 + 255) // 256 * 256
+    per_slot = (one - flags(1, 1)) // 2
+    assert per_slot == 74240 + 8 * 16 * (128 + 64) * 2
+    assert kda.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64) == (64 + 1) * 16 * per_slot + flags(1, 16)
     assert kda.chunk_prefill_workspace_size(3, 100, 2, 64, 64, 32) > 0
     for bad in [(1, 64, 1, 48, 48, 64), (1, 64, 1, 128, 64, 64), (1, 64, 1, 128, 128, 48),
                 (-1, 64, 1, 128, 128, 64), (1, 64, 0, 128, 128, 64)]:
