@@ -40,12 +40,12 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "f136a9f7806dcfb6a5b36955a9d09bd60590535c51e71a0175cbdb83b52dc51f",
-              88383210, 74113331),
-    "chain": (_PREFILL_SRC, "f136a9f7806dcfb6a5b36955a9d09bd60590535c51e71a0175cbdb83b52dc51f",
-              75168018, 18020864),
-    "decode": (_DECODE_SRC, "793b8b75d03969d4e3dce510735401b11731f26dedb9d9d875c1cf3299173e77",
-               548211414, 538968064),
+    "intra": (_PREFILL_SRC, "3085f456663abd88188dfbaf71e7f3ffbb540a2dd3d39d599750fbe4e234fe86",
+              88383488, 73925120),
+    "chain": (_PREFILL_SRC, "3085f456663abd88188dfbaf71e7f3ffbb540a2dd3d39d599750fbe4e234fe86",
+              125572915, 68166963),
+    "decode": (_DECODE_SRC, "fa7de6ad27a89ac1caa9e5cea396351bd819ce2d5889c4a9d6de2cbff7eb9a57",
+               548016128, 539395994),
 }
 
 
