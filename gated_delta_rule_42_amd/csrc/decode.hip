@@ -58,6 +58,7 @@ void kda_decode_kernel(const AT* __restrict__ q, const AT* __restrict__ k,
     using Sh = DecodeShape<DK, DV>;
     __shared__ float s_q[DK], s_k[DK], s_a[DK];
     __shared__ float s_u[Sh::RG][DV], s_w[Sh::RG][DV], s_kq[Sh::RG];
+    __shared__ float s_ut[DV], s_wt[DV], s_kqt;
     __shared__ float s_norm[2];
 
     const int b = blockIdx.x / heads, h = blockIdx.x % heads;
@@ -133,17 +134,31 @@ void kda_decode_kernel(const AT* __restrict__ q, const AT* __restrict__ k,
         if (c0 == 0) s_kq[rg] = kq;
         __syncthreads();
 
-        float d[4], o[4];
-        float kqt = 0.0f;
+        // Column totals over the row groups, each summed once (fixed order).
+        for (int i = tid; i < 2 * DV + 1; i += Sh::NT) {
+            float acc = 0.0f;
+            if (i < DV) {
 #pragma unroll
-        for (int gi = 0; gi < Sh::RG; ++gi) kqt += s_kq[gi];
+                for (int gi = 0; gi < Sh::RG; ++gi) acc += s_u[gi][i];
+                s_ut[i] = acc;
+            } else if (i < 2 * DV) {
+#pragma unroll
+                for (int gi = 0; gi < Sh::RG; ++gi) acc += s_w[gi][i - DV];
+                s_wt[i - DV] = acc;
+            } else {
+#pragma unroll
+                for (int gi = 0; gi < Sh::RG; ++gi) acc += s_kq[gi];
+                s_kqt = acc;
+            }
+        }
+        __syncthreads();
+
+        float d[4], o[4];
+        const float kqt = s_kqt;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            float ut = 0.0f, wt = 0.0f;
-#pragma unroll
-            for (int gi = 0; gi < Sh::RG; ++gi) { ut += s_u[gi][c0 + c]; wt += s_w[gi][c0 + c]; }
-            d[c] = bt * (vv[c] - ut);
-            o[c] = scale * (wt + d[c] * kqt);
+            d[c] = bt * (vv[c] - s_ut[c0 + c]);
+            o[c] = scale * (s_wt[c0 + c] + d[c] * kqt);
         }
         if (rg == 0) {
             AT* ob = out + row * os + (int64_t)h * DV;
