@@ -14,7 +14,8 @@ activations (each ~80 MB).  The same line carries:
   * spec: speculative decode of the same batch with 4 draft tokens per row
     (draft tokens/s; state after every token written), and its commit;
   * pipeline: tokens/s of one 4096-token call of the long-context pipeline
-    (conv1d -> prefill with q/k L2 norm, bf16 state, checkpoint -> gated RMSNorm);
+    (conv1d -> prefill with q/k L2 norm, bf16 state, checkpoint -> gated RMSNorm),
+    with the conv fused into the prefill, and the unfused calls beside it;
   * roofline objects (algorithmic bytes / measured time against 8 TB/s);
   * cpu_baseline: the fp64 oracle timed on the host on the same prefill
     workload (bounded to ~10 s).
@@ -222,7 +223,7 @@ def bench_pipeline(steps: int, warmup: int):
                      device=dev)
     hd = H * d
 
-    def call(i):
+    def unfused(i):
         kda.causal_conv1d(x, w, cu, conv_pool, slot, y)
         kda.chunk_prefill(y[:, :hd].view(T, H, d), y[:, hd:2 * hd].view(T, H, d),
                           y[:, 2 * hd:].view(T, H, d), g, beta, cu, pool, slot, o, workspace=ws,
@@ -230,8 +231,15 @@ def bench_pipeline(steps: int, warmup: int):
                           flags=kda.KDA_FLAG_QK_L2NORM)
         kda.gated_rmsnorm(o, gate, z, weight=nw, eps=lc.eps)
 
-    ms, wall, _ = time_calls(call, steps, warmup)
-    return lc, ms, wall
+    def fused(i):
+        kda.conv_chunk_prefill(x, w, conv_pool, g, beta, cu, pool, slot, o, workspace=ws,
+                               checkpoints=ckpt, ckpt_interval=T, chunk_size=64,
+                               flags=kda.KDA_FLAG_QK_L2NORM)
+        kda.gated_rmsnorm(o, gate, z, weight=nw, eps=lc.eps)
+
+    ums, _, _ = time_calls(unfused, steps, warmup)
+    ms, wall, _ = time_calls(fused, steps, warmup)
+    return lc, ms, wall, ums
 
 
 def bench_copy(steps: int, warmup: int, nbytes: int = 1 << 30):
@@ -347,10 +355,13 @@ def main() -> int:
                        "achieved": cbytes / (cms * 1e-3) / 1e9, "unit": "GB/s",
                        "alg_bytes": cbytes}}
     if args.only in (None, "pipeline"):
-        lc, pms, pwall = bench_pipeline(K, W)
+        lc, pms, pwall, ums = bench_pipeline(K, W)
         result["pipeline"] = {
             "value": lc.T_call / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms,
-            "steps": K, "workload": lc.name + " (one 4096-token call per step)"}
+            "steps": K, "workload": lc.name + " (one 4096-token call per step)",
+            "front_end": "fused conv1d + prefill (kda_conv_chunk_prefill)",
+            "unfused": {"value": lc.T_call / (ums * 1e-3), "ms_per_step": ums,
+                        "front_end": "kda_causal_conv1d then kda_chunk_prefill"}}
     if args.only == "copy":
         result["copy"] = bench_copy(K, W)
     if args.only in (None, "prefill") and not args.no_cpu_baseline:

@@ -61,7 +61,12 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
     return kda::prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv, chunk_size);
 }
 
-kda_status_t kda_chunk_prefill(
+namespace {
+
+// Checks and fills everything the two prefill entry points share.  q, k, v
+// may be null when total_tokens is 0.
+kda_status_t prefill_common(
+    kda::PrefillArgs& a,
     const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
     int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
     const float* g, const float* beta,
@@ -72,7 +77,7 @@ kda_status_t kda_chunk_prefill(
     void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
     float scale, int32_t chunk_size, uint32_t flags,
     void* out, int64_t out_stride_t,
-    void* workspace, size_t workspace_bytes, void* stream)
+    void* workspace, size_t workspace_bytes)
 {
     if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || num_slots < 0 ||
         ckpt_capacity < 0 || ckpt_interval < 0)
@@ -99,7 +104,6 @@ kda_status_t kda_chunk_prefill(
     if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
         return KDA_ERR_INVALID_ARG;
 
-    kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v;
     a.q_stride = q_stride_t; a.k_stride = k_stride_t; a.v_stride = v_stride_t;
     a.g = g; a.beta = beta;
@@ -114,11 +118,77 @@ kda_status_t kda_chunk_prefill(
     a.out = out; a.out_stride = out_stride_t;
     a.workspace = workspace;
     a.act = act_dtype; a.state = state_dtype;
+    a.conv_w = a.conv_b = nullptr; a.conv_state = nullptr;
+    a.conv_width = 0; a.conv_flags = 0;
     a.ev[0] = a.ev[1] = a.ev[2] = nullptr;
     if (g_timing.events && g_timing.used < g_timing.capacity) {
         hipEvent_t* ev = g_timing.events + 3 * g_timing.used++;
         a.ev[0] = ev[0]; a.ev[1] = ev[1]; a.ev[2] = ev[2];
     }
+    return KDA_OK;
+}
+
+}  // namespace
+
+kda_status_t kda_chunk_prefill(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda::PrefillArgs a;
+    const kda_status_t st = prefill_common(
+        a, q, k, v, act_dtype, q_stride_t, k_stride_t, v_stride_t, g, beta, cu_seqlens, num_seqs,
+        total_tokens, num_heads, dk, dv, state_pool, state_dtype, num_slots, state_indices,
+        has_initial_state, checkpoints, ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out,
+        out_stride_t, workspace, workspace_bytes);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_conv_chunk_prefill(
+    const void* x, int64_t x_stride_t, kda_dtype_t act_dtype,
+    const void* conv_weight, const void* conv_bias, int32_t conv_width, uint32_t conv_flags,
+    void* conv_state_pool,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (conv_width < 2 || conv_width > 8) return KDA_ERR_UNSUPPORTED;
+    if (conv_flags & ~KDA_CONV_SILU) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(act_dtype)) return KDA_ERR_INVALID_ARG;
+    const int64_t hd = (int64_t)num_heads * dk;
+    if (num_heads > 0 && x_stride_t < 3 * hd) return KDA_ERR_INVALID_ARG;
+    const size_t es = act_dtype == KDA_BF16 ? 2 : 4;
+    const char* xb = static_cast<const char*>(x);
+    const bool have_x = total_tokens > 0 && x;
+    kda::PrefillArgs a;
+    const kda_status_t st = prefill_common(
+        a, x, have_x ? xb + hd * es : nullptr, have_x ? xb + 2 * hd * es : nullptr, act_dtype,
+        x_stride_t, x_stride_t, x_stride_t, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+        dk, dv, state_pool, state_dtype, num_slots, state_indices, has_initial_state, checkpoints,
+        ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out, out_stride_t, workspace,
+        workspace_bytes);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    if (total_tokens > 0 && !conv_weight) return KDA_ERR_INVALID_ARG;
+    if (num_slots > 0 && !conv_state_pool) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(conv_weight) || !aligned16(conv_bias) || !aligned16(conv_state_pool))
+        return KDA_ERR_INVALID_ARG;
+    a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state_pool;
+    a.conv_width = conv_width; a.conv_flags = conv_flags;
     return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

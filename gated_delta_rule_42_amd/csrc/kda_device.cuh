@@ -142,6 +142,15 @@ __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, const f32x4& c
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// SiLU(a) = a / (1 + e^{-a}), with the hardware reciprocal (within 1 ulp)
+// in place of a correctly rounded division.  The conv kernel and the conv
+// front end of the prefill both use this one definition, so their outputs
+// agree bit for bit.
+__device__ __forceinline__ float silu_f32(float a)
+{
+    return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8])
 {
     bf16x8 r;

@@ -50,6 +50,11 @@ struct PrefillArgs {
     void* out; int64_t out_stride;
     void* workspace;
     kda_dtype_t act, state;
+    // Fused front end (conv_width > 0): q, k, v point into the packed
+    // projection x and are taken through the causal conv1d first; its state
+    // pool is indexed like the state pool (same slots, has_init, num_slots).
+    const void* conv_w; const void* conv_b; void* conv_state;
+    int32_t conv_width; uint32_t conv_flags;
     // Optional timing events (all null, or all valid): recorded on the stream
     // before the intra-chunk kernel, between it and the chain kernel, and
     // after the chain kernel.
@@ -83,5 +88,7 @@ struct ConvArgs {
     kda_dtype_t dtype;
 };
 hipError_t launch_causal_conv1d(const ConvArgs& a, hipStream_t stream);
+// Only the conv state update of launch_causal_conv1d (y is not written).
+hipError_t launch_conv_state_update(const ConvArgs& a, hipStream_t stream);
 
 }  // namespace kda

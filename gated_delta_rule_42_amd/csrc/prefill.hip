@@ -256,13 +256,152 @@ __device__ __forceinline__ bf16x8 identity_half(int half, int lane)
 //   5. W = T K~ and U = T V on bf16 MFMA from LDS tiles, K~^T and V^T having
 //      been transposed with identity MFMA products in step 2.
 // Record stores are 8- or 16-byte vector stores in the swizzled layout.
-template <int D, int BT, typename AT>
+// Causal conv1d of the fused front end (the operation of kda_causal_conv1d on
+// the packed [q | k | v] projection), evaluated where the intra kernel loads
+// its activations.
+template <typename AT>
+struct ConvIn {
+    const AT* w;            // [channels, width]
+    const AT* b;            // [channels] or null
+    const AT* state;        // [num_slots, width - 1, channels] (row width - 2 = newest)
+    const uint8_t* has_init;    // [num_seqs] or null (= all 1)
+    int64_t num_slots;
+    int64_t channels;       // 3 H d
+    int width;              // 2 .. 8
+    bool silu;
+};
+
+constexpr int kMaxConvWidth = 8;
+
+// Eight consecutive activations as raw 32-bit words (bf16 pairs or fp32), the
+// unit the conv front end moves between lanes.
+template <typename AT>
+struct Raw8 {
+    static constexpr int N = 2 * (int)sizeof(AT);
+    uint32_t u[N];
+};
+
+template <typename AT>
+__device__ __forceinline__ Raw8<AT> load_raw8(const AT* p)
+{
+    Raw8<AT> r;
+    const uint4* s = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < Raw8<AT>::N / 4; ++i) {
+        const uint4 t = s[i];
+        r.u[4 * i] = t.x; r.u[4 * i + 1] = t.y; r.u[4 * i + 2] = t.z; r.u[4 * i + 3] = t.w;
+    }
+    return r;
+}
+
+template <typename AT>
+__device__ __forceinline__ Raw8<AT> zero_raw8()
+{
+    Raw8<AT> r;
+#pragma unroll
+    for (int i = 0; i < Raw8<AT>::N; ++i) r.u[i] = 0u;
+    return r;
+}
+
+__device__ __forceinline__ void widen8(const Raw8<bf16>& r, float (&x)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r.u[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r.u[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void widen8(const Raw8<float>& r, float (&x)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(r.u[i]);
+}
+
+// The conv inputs of one 8-channel group for this lane's token row r: its own
+// row (token tr) and, in lanes 17 - W .. 15 of each 16-lane row group, the row
+// 16 tokens earlier (token tr - 16, which may precede the sequence and then
+// comes from its conv state).  Tap m of lane l then reads row r - m from lane
+// (l - m) mod 16 of a DPP row rotation: the own row of lane l - m when l >= m,
+// else the early row of lane l + 16 - m, which is token tr - m as well.
+template <typename AT>
+struct ConvRows {
+    Raw8<AT> own, early;
+};
+
+template <typename AT>
+__device__ __forceinline__ void conv_fetch(ConvRows<AT>& cr, const AT* __restrict__ xp, int64_t xs,
+                                           int64_t tr, bool own_ok, bool early_ok, int64_t s0,
+                                           const AT* __restrict__ st_row0, int64_t channels,
+                                           int width)
+{
+    cr.own = own_ok ? load_raw8(xp + tr * xs) : zero_raw8<AT>();
+    cr.early = zero_raw8<AT>();
+    if (early_ok) {
+        const int64_t p = tr - 16;
+        if (p >= s0)
+            cr.early = load_raw8(xp + p * xs);
+        else if (st_row0)                         // s0 - p is 1 .. width - 1 here
+            cr.early = load_raw8(st_row0 + (int64_t)((width - 1) - (s0 - p)) * channels);
+    }
+}
+
+// Taps M, M - 1, .. 0 of the conv (tap m reads row r - m with weight
+// W - 1 - m); taps at or past the width are skipped.
+template <int M, int D, typename AT>
+__device__ __forceinline__ void conv_taps(float (&acc)[8], const ConvRows<AT>& cr, const AT* wt,
+                                          int width, int l16)
+{
+    if (M <= width - 1) {
+        float xv[8], wv[8];
+        if constexpr (M == 0) {
+            widen8(cr.own, xv);
+        } else {
+            Raw8<AT> t;
+            const bool early = l16 >= 16 - M;
+#pragma unroll
+            for (int i = 0; i < Raw8<AT>::N; ++i)
+                t.u[i] = (uint32_t)__builtin_amdgcn_mov_dpp(
+                    (int)(early ? cr.early.u[i] : cr.own.u[i]), 0x120 + M /* row_ror:M */, 0xF, 0xF,
+                    false);
+            widen8(t, xv);
+        }
+        load8(wt + (width - 1 - M) * D, wv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wv[i] * xv[i];
+    }
+    if constexpr (M > 0) conv_taps<M - 1, D>(acc, cr, wt, width, l16);
+}
+
+// Conv output of the group: bias, then the taps from the oldest input (row
+// r - (W-1)) to the current one, then SiLU, rounded to bf16 as the
+// activations are.  The same operations in the same order as the conv kernel.
+// wt: the group's tap-major weights in LDS (tap j at wt[j * D]).
+template <int D, typename AT>
+__device__ __forceinline__ bf16x8 conv_eval(const ConvRows<AT>& cr, const AT* bias, const AT* wt,
+                                            int width, bool silu, int l16)
+{
+    float acc[8];
+    if (bias) {
+        load8(bias, acc);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    }
+    conv_taps<kMaxConvWidth - 1, D>(acc, cr, wt, width, l16);
+    if (silu) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = silu_f32(acc[i]);
+    }
+    return pack_bf16x8(acc);
+}
+
+template <int D, int BT, typename AT, bool CONV>
 __global__ __launch_bounds__(kThreads, 2)
 void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* __restrict__ v,
                   int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ g,
                   const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
                   int heads, const int32_t* __restrict__ slots, uint32_t flags,
-                  uint8_t* __restrict__ ws, int64_t flag_off, int64_t n_flags)
+                  uint8_t* __restrict__ ws, int64_t flag_off, int64_t n_flags, ConvIn<AT> cv)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NKK = P::NKK_K;
@@ -294,6 +433,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     __shared__ __attribute__((aligned(16))) float sAft[4][DKP];          // e^{G_C - G_b}
     __shared__ __attribute__((aligned(16))) float sInv[4][DKP];          // e^{-G_b}
     __shared__ __attribute__((aligned(16))) float sBeta[BTP];
+    __shared__ __attribute__((aligned(16))) AT sCw[CONV ? 3 * kMaxConvWidth * D : 1];   // conv weights
 
     const int x = blockIdx.x, h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -341,17 +481,68 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
         }
     }
     if (valid) b_r = beta[tr * heads + h];
+    if constexpr (CONV) {
+        // q, k, v are the conv outputs of channels h d + c of the packed
+        // projection's three parts (q = x, k = x + H d, v = x + 2 H d).
+        const int W = cv.width;
+        const int64_t hd = (int64_t)heads * D;
+        // Weights of this head's channels, tap-major per part: sCw[(part W + j) D + c].
+        for (int e = tid; e < 3 * W * D; e += kThreads) {
+            const int c = e % D, pj = e / D;
+            const int part = pj / W, j = pj - part * W;
+            sCw[e] = cv.w[(part * hd + (int64_t)h * D + c) * W + j];
+        }
+        const int64_t s0 = cu[seq];
+        const int cslot = slots[seq];
+        const bool cinit = cslot < cv.num_slots && (cv.has_init ? cv.has_init[seq] != 0 : true);
+        const AT* st = cinit ? cv.state + (int64_t)cslot * (W - 1) * cv.channels : nullptr;
+        const bool early_lane = tok_wave && l16 >= 17 - W && r - 16 < len;
+        const AT* xpart[3] = {q, k, v};
+        const int64_t xstr[3] = {qs, ks, vs};
+        auto fetch = [&](int part, ConvRows<AT> (&cr)[NKK]) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        const int c0 = 32 * kk + 8 * g4;
-        const bool ok = valid && c0 < D;
-        kk8[kk] = ok ? load8_bf16(k + tr * ks + (int64_t)h * D + c0) : bf16x8{};
-        kq[kk] = ok ? load8_bf16(q + tr * qs + (int64_t)h * D + c0) : bf16x8{};
-    }
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int c0 = 32 * kk + 8 * g4;
+                const bool ok = c0 < D;
+                const int64_t ch = (int64_t)h * D + c0;
+                conv_fetch(cr[kk], xpart[part] + ch, xstr[part], tr, valid && ok, early_lane && ok, s0,
+                           st ? st + part * hd + ch : nullptr, cv.channels, W);
+            }
+        };
+        auto eval = [&](int part, const ConvRows<AT> (&cr)[NKK], bf16x8 (&dst)[NKK]) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        const int c0 = 32 * kk + 8 * g4;
-        kv[kk] = (valid && c0 < D) ? load8_bf16(v + tr * vs + (int64_t)h * D + c0) : bf16x8{};
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int c0 = 32 * kk + 8 * g4;
+                const bool ok = valid && c0 < D;
+                const int cc = c0 < D ? c0 : 0;
+                const bf16x8 y = conv_eval<D>(cr[kk], cv.b ? cv.b + part * hd + (int64_t)h * D + cc : nullptr,
+                                              sCw + part * W * D + cc, W, cv.silu, l16);
+                dst[kk] = ok ? y : bf16x8{};
+            }
+        };
+        // k first, then q, then v (the order of first use); each part's rows
+        // are fetched one part ahead of its evaluation.
+        ConvRows<AT> ra[NKK], rb[NKK];
+        fetch(1, ra);
+        lds_barrier();                       // the staged weights
+        fetch(0, rb);
+        eval(1, ra, kk8);
+        fetch(2, ra);
+        eval(0, rb, kq);
+        eval(2, ra, kv);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int c0 = 32 * kk + 8 * g4;
+            const bool ok = valid && c0 < D;
+            kk8[kk] = ok ? load8_bf16(k + tr * ks + (int64_t)h * D + c0) : bf16x8{};
+            kq[kk] = ok ? load8_bf16(q + tr * qs + (int64_t)h * D + c0) : bf16x8{};
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int c0 = 32 * kk + 8 * g4;
+            kv[kk] = (valid && c0 < D) ? load8_bf16(v + tr * vs + (int64_t)h * D + c0) : bf16x8{};
+        }
     }
     if (tok_wave && g4 == 0) sBeta[r] = b_r;
     if (BTP > BT && tid < BTP - BT) sBeta[BT + tid] = 0.0f;
@@ -1052,13 +1243,43 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     if (a.total_tokens > 0) {
-        hipLaunchKernelGGL((intra_kernel<D, BT, AT>), dim3((unsigned)chunks, (unsigned)a.heads),
-                           dim3(kThreads), 0, stream, static_cast<const AT*>(a.q),
-                           static_cast<const AT*>(a.k), static_cast<const AT*>(a.v), a.q_stride,
-                           a.k_stride, a.v_stride, a.g, a.beta, a.cu_seqlens, a.num_seqs, a.heads,
-                           a.slots, a.flags, static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags);
-        const hipError_t e = hipGetLastError();
+        ConvIn<AT> cv;
+        cv.w = static_cast<const AT*>(a.conv_w);
+        cv.b = static_cast<const AT*>(a.conv_b);
+        cv.state = static_cast<const AT*>(a.conv_state);
+        cv.has_init = a.has_init;
+        cv.num_slots = a.num_slots;
+        cv.channels = 3 * (int64_t)a.heads * D;
+        cv.width = a.conv_width;
+        cv.silu = (a.conv_flags & KDA_CONV_SILU) != 0;
+        const dim3 grid((unsigned)chunks, (unsigned)a.heads);
+        if (a.conv_width > 0)
+            hipLaunchKernelGGL((intra_kernel<D, BT, AT, true>), grid, dim3(kThreads), 0, stream,
+                               static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
+                               static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
+                               a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
+                               static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags, cv);
+        else
+            hipLaunchKernelGGL((intra_kernel<D, BT, AT, false>), grid, dim3(kThreads), 0, stream,
+                               static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
+                               static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
+                               a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
+                               static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags, cv);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.conv_width > 0) {
+            // The conv state's new rows, once the intra kernel has read the old ones.
+            ConvArgs c;
+            c.x = a.q; c.x_stride = a.q_stride;
+            c.weight = a.conv_w; c.bias = a.conv_b;
+            c.state = a.conv_state; c.num_slots = a.num_slots;
+            c.cu_seqlens = a.cu_seqlens; c.slots = a.slots; c.has_init = a.has_init;
+            c.num_seqs = a.num_seqs; c.total_tokens = a.total_tokens;
+            c.channels = (int32_t)cv.channels; c.width = a.conv_width; c.flags = a.conv_flags;
+            c.y = nullptr; c.y_stride = 0; c.dtype = a.act;
+            e = launch_conv_state_update(c, stream);
+            if (e != hipSuccess) return e;
+        }
     }
     if (a.ev[1]) {
         const hipError_t e = hipEventRecord(a.ev[1], stream);

@@ -55,6 +55,13 @@ def _load() -> ctypes.CDLL:
         vp, i32, i64, vp, vp,
         vp, i64, i32,
         f32, i32, u32, vp, i64, vp, sz, vp]
+    lib.kda_conv_chunk_prefill.restype = i32
+    lib.kda_conv_chunk_prefill.argtypes = [
+        vp, i64, i32, vp, vp, i32, u32, vp, vp, vp,
+        vp, i32, i64, i32, i32, i32,
+        vp, i32, i64, vp, vp,
+        vp, i64, i32,
+        f32, i32, u32, vp, i64, vp, sz, vp]
     lib.kda_recurrent_decode.restype = i32
     lib.kda_recurrent_decode.argtypes = [
         vp, vp, vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, i32,
@@ -171,6 +178,58 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, 
         _ptr(out), _token_stride(out, "out"),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("kda_chunk_prefill", status)
+
+
+def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, state_pool,
+                       state_indices, out, *, conv_bias=None, silu: bool = True, workspace=None,
+                       has_initial_state=None, checkpoints=None, ckpt_interval: int = 0,
+                       scale: float = 1.0, chunk_size: int = 64, flags: int = 0,
+                       stream=None) -> None:
+    """kda_conv_chunk_prefill.  x [T, 3*H*d] packed q|k|v before the conv
+    (token stride allowed, channels contiguous); conv_weight [3Hd, W];
+    conv_state_pool [slots, W-1, 3Hd] (updated in place); out [T,H,d]; the
+    rest as chunk_prefill."""
+    T, C = x.shape
+    H, dv = out.shape[1], out.shape[2]
+    dk = dv
+    if C != 3 * H * dk:
+        raise ValueError("x must hold 3*H*d channels")
+    if x.stride(1) != 1:
+        raise ValueError("x needs contiguous channels")
+    W = conv_weight.shape[1]
+    N = state_indices.numel()
+    _contig(conv_weight, "conv_weight", x.dtype)
+    if conv_bias is not None:
+        _contig(conv_bias, "conv_bias", x.dtype)
+    if not conv_state_pool.is_contiguous() or conv_state_pool.dtype != x.dtype:
+        raise ValueError("conv_state_pool must be contiguous with x's dtype")
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    _contig(cu_seqlens, "cu_seqlens", torch.int32)
+    _contig(state_indices, "state_indices", torch.int32)
+    if has_initial_state is not None:
+        _contig(has_initial_state, "has_initial_state", torch.uint8)
+    if not state_pool.is_contiguous():
+        raise ValueError("state_pool must be contiguous")
+    need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    cap = 0
+    if checkpoints is not None:
+        if not checkpoints.is_contiguous() or checkpoints.dtype != state_pool.dtype:
+            raise ValueError("checkpoints must be contiguous with the state dtype")
+        cap = checkpoints.shape[0]
+    status = _lib.kda_conv_chunk_prefill(
+        _ptr(x), x.stride(0), _dtype(x), _ptr(conv_weight), _ptr(conv_bias), W,
+        KDA_CONV_SILU if silu else 0, _ptr(conv_state_pool),
+        _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+        _ptr(state_pool), _dtype(state_pool), state_pool.shape[0] if state_pool.dim() else 0,
+        _ptr(state_indices), _ptr(has_initial_state),
+        _ptr(checkpoints), cap, int(ckpt_interval),
+        float(scale), int(chunk_size), int(flags),
+        _ptr(out), _token_stride(out, "out"),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("kda_conv_chunk_prefill", status)
 
 
 def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, out, *, scale: float = 1.0,

@@ -221,6 +221,40 @@ kda_status_t kda_causal_conv1d(
     void* y, int64_t y_stride_t, void* stream);
 
 /*
+ * Fused front end + chunk prefill: kda_causal_conv1d over the packed
+ * projection x = [q | k | v] followed by kda_chunk_prefill on its three parts,
+ * with the convolution evaluated where the prefill loads its activations, so
+ * the conv output never goes to memory (page "Add Kimi K3 KDA execution", KDA
+ * execution steps 2-3: run the causal convolution and update its cache, then
+ * the chunked prefill; What this PR does: causal-convolution state packing).
+ *   x        [total_tokens, 3 H d] of act_dtype, token stride x_stride_t:
+ *            channels [0, Hd) are q, [Hd, 2Hd) k, [2Hd, 3Hd) v (head-major d)
+ *   conv_weight [3 H d, conv_width] of act_dtype; conv_bias [3 H d] or NULL
+ *   conv_width  2 .. 8;  conv_flags  KDA_CONV_SILU
+ *   conv_state_pool [num_slots, conv_width - 1, 3 H d] of act_dtype, indexed
+ *            like state_pool (state_indices, has_initial_state, num_slots);
+ *            after the call it holds each sequence's last conv_width - 1 rows
+ *            of x, exactly as kda_causal_conv1d leaves it.
+ * All other arguments, the workspace and the results are those of
+ * kda_chunk_prefill (flags KDA_FLAG_QK_L2NORM normalises the conv outputs
+ * q, k).  The result equals, bit for bit, kda_causal_conv1d into a buffer y
+ * followed by kda_chunk_prefill reading q, k, v from y.
+ */
+kda_status_t kda_conv_chunk_prefill(
+    const void* x, int64_t x_stride_t, kda_dtype_t act_dtype,
+    const void* conv_weight, const void* conv_bias, int32_t conv_width, uint32_t conv_flags,
+    void* conv_state_pool,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Speculative multi-token decode (page "[Feature][KDA] Add Kimi K3 KDA
  * execution", Metadata construction: speculative decode is a path of its own
  * next to chunk prefill and recurrent decode; page "FlashKDA kernel upgrade

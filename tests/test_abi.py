@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_chunk_prefill", "kda_recurrent_decode", "kda_gated_rmsnorm",
                  "kda_causal_conv1d", "kda_chunk_prefill_workspace_size",
-                 "kda_spec_decode", "kda_spec_commit",
+                 "kda_conv_chunk_prefill", "kda_spec_decode", "kda_spec_commit",
                  "kda_abi_version", "kda_status_string"):
         assert want in names
 
@@ -109,6 +109,36 @@ def test_prefill_validation(lib):
     assert _prefill(lib, wsb=100) == K.KDA_ERR_WORKSPACE_TOO_SMALL
     need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
     assert _prefill(lib, wsb=need, ws=FAKE + 16) == K.KDA_ERR_INVALID_ARG   # 256-B alignment
+
+
+def _conv_prefill(lib, **over):
+    a = dict(x=FAKE, xs=6144, act=1, w=FAKE, b=None, W=4, cflags=1, cpool=FAKE, g=FAKE,
+             beta=FAKE, cu=FAKE, n=1, T=64, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=4,
+             idx=FAKE, hi=None, ck=None, cap=0, interval=0, scale=1.0, C=64, flags=1,
+             out=FAKE, os=2048, ws=FAKE, wsb=0, stream=None)
+    a.update(over)
+    return lib.kda_conv_chunk_prefill(*a.values())
+
+
+def test_conv_prefill_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+    need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
+    assert _conv_prefill(lib, n=0) == K.KDA_OK                          # nothing to do
+    assert _conv_prefill(lib, W=1) == K.KDA_ERR_UNSUPPORTED
+    assert _conv_prefill(lib, W=9) == K.KDA_ERR_UNSUPPORTED
+    assert _conv_prefill(lib, cflags=2) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, act=7) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, xs=6000) == K.KDA_ERR_INVALID_ARG         # < 3 H dk
+    assert _conv_prefill(lib, xs=6148) == K.KDA_ERR_INVALID_ARG         # not a multiple of 8
+    assert _conv_prefill(lib, x=None) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, dk=48, dv=48, xs=3 * 16 * 48) == K.KDA_ERR_UNSUPPORTED
+    assert _conv_prefill(lib, wsb=100) == K.KDA_ERR_WORKSPACE_TOO_SMALL
+    # Past the prefill checks (workspace large enough), the conv arguments.
+    assert _conv_prefill(lib, wsb=need, w=None) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, wsb=need, w=FAKE + 2) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, wsb=need, b=FAKE + 4) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, wsb=need, cpool=None) == K.KDA_ERR_INVALID_ARG
+    assert _conv_prefill(lib, wsb=need, cpool=FAKE + 8) == K.KDA_ERR_INVALID_ARG
 
 
 def test_decode_validation(lib):
