@@ -199,31 +199,6 @@ hipError_t launch_typed(const ConvArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int W, typename T>
-hipError_t launch_state_only(const ConvArgs& a, hipStream_t stream)
-{
-    const unsigned gc = (unsigned)((a.channels / 8 + kConvBlock - 1) / kConvBlock);
-    hipLaunchKernelGGL((state_kernel<W, T>), dim3((unsigned)a.num_seqs, gc), dim3(kConvBlock), 0,
-                       stream, static_cast<const T*>(a.x), a.x_stride, static_cast<T*>(a.state),
-                       a.num_slots, a.cu_seqlens, a.slots, a.has_init, a.channels);
-    return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_state_width(const ConvArgs& a, hipStream_t stream)
-{
-    switch (a.width) {
-        case 2: return launch_state_only<2, T>(a, stream);
-        case 3: return launch_state_only<3, T>(a, stream);
-        case 4: return launch_state_only<4, T>(a, stream);
-        case 5: return launch_state_only<5, T>(a, stream);
-        case 6: return launch_state_only<6, T>(a, stream);
-        case 7: return launch_state_only<7, T>(a, stream);
-        case 8: return launch_state_only<8, T>(a, stream);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 template <typename T>
 hipError_t launch_width(const ConvArgs& a, hipStream_t stream)
 {
@@ -240,12 +215,6 @@ hipError_t launch_width(const ConvArgs& a, hipStream_t stream)
 }
 
 }  // namespace
-
-hipError_t launch_conv_state_update(const ConvArgs& a, hipStream_t stream)
-{
-    if (a.num_seqs == 0) return hipSuccess;
-    return a.dtype == KDA_BF16 ? launch_state_width<bf16>(a, stream) : launch_state_width<float>(a, stream);
-}
 
 hipError_t launch_causal_conv1d(const ConvArgs& a, hipStream_t stream)
 {

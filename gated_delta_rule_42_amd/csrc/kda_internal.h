@@ -88,7 +88,5 @@ struct ConvArgs {
     kda_dtype_t dtype;
 };
 hipError_t launch_causal_conv1d(const ConvArgs& a, hipStream_t stream);
-// Only the conv state update of launch_causal_conv1d (y is not written).
-hipError_t launch_conv_state_update(const ConvArgs& a, hipStream_t stream);
 
 }  // namespace kda

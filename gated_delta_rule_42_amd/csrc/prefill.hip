@@ -263,7 +263,7 @@ template <typename AT>
 struct ConvIn {
     const AT* w;            // [channels, width]
     const AT* b;            // [channels] or null
-    const AT* state;        // [num_slots, width - 1, channels] (row width - 2 = newest)
+    AT* state;              // [num_slots, width - 1, channels] (row width - 2 = newest)
     const uint8_t* has_init;    // [num_seqs] or null (= all 1)
     int64_t num_slots;
     int64_t channels;       // 3 H d
@@ -292,6 +292,15 @@ __device__ __forceinline__ Raw8<AT> load_raw8(const AT* p)
         r.u[4 * i] = t.x; r.u[4 * i + 1] = t.y; r.u[4 * i + 2] = t.z; r.u[4 * i + 3] = t.w;
     }
     return r;
+}
+
+template <typename AT>
+__device__ __forceinline__ void store_raw8(AT* p, const Raw8<AT>& r)
+{
+    uint4* d = reinterpret_cast<uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < Raw8<AT>::N / 4; ++i)
+        d[i] = make_uint4(r.u[4 * i], r.u[4 * i + 1], r.u[4 * i + 2], r.u[4 * i + 3]);
 }
 
 template <typename AT>
@@ -345,13 +354,32 @@ __device__ __forceinline__ void conv_fetch(ConvRows<AT>& cr, const AT* __restric
     }
 }
 
+// Element u of a 16-byte vector of AT (bf16 or fp32), widened to fp32 and
+// stored to p (u a constant after unrolling).
+__device__ __forceinline__ uint32_t vec_word(const uint4& v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+template <typename AT>
+__device__ __forceinline__ void store_elem_f32(float* p, const uint4& v, int u)
+{
+    if constexpr (sizeof(AT) == 2)
+        *p = __uint_as_float(((vec_word(v, u >> 1) >> (16 * (u & 1))) & 0xffffu) << 16);
+    else
+        *p = __uint_as_float(vec_word(v, u));
+}
+
 // Taps M, M - 1, .. 0 of the conv (tap m reads row r - m with weight
-// W - 1 - m); taps at or past the width are skipped.
-template <int M, int D, typename AT>
-__device__ __forceinline__ void conv_taps(float (&acc)[8], const ConvRows<AT>& cr, const AT* wt,
+// W - 1 - m); taps at or past the width are skipped.  WC > 0 is the width
+// known at compile time (no branches, so the weight reads of all taps are
+// issued together); WC = 0 takes it from `width`.
+template <int M, int D, int WC, typename AT>
+__device__ __forceinline__ void conv_taps(float (&acc)[8], const ConvRows<AT>& cr, const float* wt,
                                           int width, int l16)
 {
-    if (M <= width - 1) {
+    const bool live = WC > 0 ? M <= WC - 1 : M <= width - 1;
+    if (live) {
+        const int W = WC > 0 ? WC : width;
         float xv[8], wv[8];
         if constexpr (M == 0) {
             widen8(cr.own, xv);
@@ -365,19 +393,19 @@ __device__ __forceinline__ void conv_taps(float (&acc)[8], const ConvRows<AT>& c
                     false);
             widen8(t, xv);
         }
-        load8(wt + (width - 1 - M) * D, wv);
+        load8(wt + (W - 1 - M) * D, wv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += wv[i] * xv[i];
     }
-    if constexpr (M > 0) conv_taps<M - 1, D>(acc, cr, wt, width, l16);
+    if constexpr (M > 0) conv_taps<M - 1, D, WC>(acc, cr, wt, width, l16);
 }
 
 // Conv output of the group: bias, then the taps from the oldest input (row
 // r - (W-1)) to the current one, then SiLU, rounded to bf16 as the
 // activations are.  The same operations in the same order as the conv kernel.
-// wt: the group's tap-major weights in LDS (tap j at wt[j * D]).
-template <int D, typename AT>
-__device__ __forceinline__ bf16x8 conv_eval(const ConvRows<AT>& cr, const AT* bias, const AT* wt,
+// wt: the group's tap-major weights in LDS, widened to fp32 (tap j at wt[j * D]).
+template <int D, int WC, typename AT>
+__device__ __forceinline__ bf16x8 conv_eval(const ConvRows<AT>& cr, const AT* bias, const float* wt,
                                             int width, bool silu, int l16)
 {
     float acc[8];
@@ -387,7 +415,7 @@ __device__ __forceinline__ bf16x8 conv_eval(const ConvRows<AT>& cr, const AT* bi
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     }
-    conv_taps<kMaxConvWidth - 1, D>(acc, cr, wt, width, l16);
+    conv_taps<(WC > 0 ? WC : kMaxConvWidth) - 1, D, WC>(acc, cr, wt, width, l16);
     if (silu) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = silu_f32(acc[i]);
@@ -433,7 +461,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     __shared__ __attribute__((aligned(16))) float sAft[4][DKP];          // e^{G_C - G_b}
     __shared__ __attribute__((aligned(16))) float sInv[4][DKP];          // e^{-G_b}
     __shared__ __attribute__((aligned(16))) float sBeta[BTP];
-    __shared__ __attribute__((aligned(16))) AT sCw[CONV ? 3 * kMaxConvWidth * D : 1];   // conv weights
+    __shared__ __attribute__((aligned(16))) float sCw[CONV ? 3 * kMaxConvWidth * D : 1];   // conv weights
 
     const int x = blockIdx.x, h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -486,12 +514,40 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
         // projection's three parts (q = x, k = x + H d, v = x + 2 H d).
         const int W = cv.width;
         const int64_t hd = (int64_t)heads * D;
-        // Weights of this head's channels, tap-major per part: sCw[(part W + j) D + c].
-        for (int e = tid; e < 3 * W * D; e += kThreads) {
-            const int c = e % D, pj = e / D;
-            const int part = pj / W, j = pj - part * W;
-            sCw[e] = cv.w[(part * hd + (int64_t)h * D + c) * W + j];
-        }
+        // The weights of this head's channels are staged in LDS tap-major per
+        // part and widened to fp32, sCw[(part W + j) D + c].  Each part's weights are one
+        // contiguous block of D W elements (channel-major, W taps per
+        // channel), read as 16-byte vectors: all loads are issued first (with
+        // the conv rows behind them), the LDS writes come after.
+        constexpr int kVec = 16 / (int)sizeof(AT);
+        constexpr int kWIt = (3 * kMaxConvWidth * D / kVec + kThreads - 1) / kThreads;
+        const int per_part = W * D / kVec;
+        uint4 wreg[kWIt];
+        auto wload = [&]() {
+#pragma unroll
+            for (int i = 0; i < kWIt; ++i) {
+                const int e = tid + i * kThreads;
+                if (e < 3 * per_part) {
+                    const int part = e / per_part, o = e - part * per_part;
+                    wreg[i] = *reinterpret_cast<const uint4*>(cv.w + (part * hd + (int64_t)h * D) * W +
+                                                              (int64_t)o * kVec);
+                }
+            }
+        };
+        auto wstore = [&]() {
+#pragma unroll
+            for (int i = 0; i < kWIt; ++i) {
+                const int e = tid + i * kThreads;
+                if (e < 3 * per_part) {
+                    const int part = e / per_part, o = e - part * per_part;
+#pragma unroll
+                    for (int u = 0; u < kVec; ++u) {
+                        const int f = o * kVec + u, c = f / W, j = f - c * W;
+                        store_elem_f32<AT>(sCw + (part * W + j) * D + c, wreg[i], u);
+                    }
+                }
+            }
+        };
         const int64_t s0 = cu[seq];
         const int cslot = slots[seq];
         const bool cinit = cslot < cv.num_slots && (cv.has_init ? cv.has_init[seq] != 0 : true);
@@ -509,27 +565,55 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                            st ? st + part * hd + ch : nullptr, cv.channels, W);
             }
         };
-        auto eval = [&](int part, const ConvRows<AT> (&cr)[NKK], bf16x8 (&dst)[NKK]) {
+        auto eval_w = [&](auto wc, int part, const ConvRows<AT> (&cr)[NKK], bf16x8 (&dst)[NKK]) {
+            constexpr int WC = decltype(wc)::value;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int c0 = 32 * kk + 8 * g4;
                 const bool ok = valid && c0 < D;
                 const int cc = c0 < D ? c0 : 0;
-                const bf16x8 y = conv_eval<D>(cr[kk], cv.b ? cv.b + part * hd + (int64_t)h * D + cc : nullptr,
-                                              sCw + part * W * D + cc, W, cv.silu, l16);
+                const bf16x8 y = conv_eval<D, WC>(cr[kk], cv.b ? cv.b + part * hd + (int64_t)h * D + cc : nullptr,
+                                                  sCw + part * W * D + cc, W, cv.silu, l16);
                 dst[kk] = ok ? y : bf16x8{};
             }
         };
-        // k first, then q, then v (the order of first use); each part's rows
-        // are fetched one part ahead of its evaluation.
-        ConvRows<AT> ra[NKK], rb[NKK];
-        fetch(1, ra);
-        lds_barrier();                       // the staged weights
-        fetch(0, rb);
-        eval(1, ra, kk8);
-        fetch(2, ra);
-        eval(0, rb, kq);
-        eval(2, ra, kv);
+        // Widths 2 .. 4 (the common short convolutions) with the width fixed
+        // at compile time; wider ones through the general path.
+        auto eval = [&](int part, const ConvRows<AT> (&cr)[NKK], bf16x8 (&dst)[NKK]) {
+            switch (W) {
+                case 2: eval_w(std::integral_constant<int, 2>{}, part, cr, dst); break;
+                case 3: eval_w(std::integral_constant<int, 3>{}, part, cr, dst); break;
+                case 4: eval_w(std::integral_constant<int, 4>{}, part, cr, dst); break;
+                default: eval_w(std::integral_constant<int, 0>{}, part, cr, dst); break;
+            }
+        };
+        // k is evaluated first, then q, then v (the order of first use).
+        if constexpr (sizeof(AT) == 2) {
+            // All rows are requested before the first evaluation, so the
+            // chunk waits for one round of load latency.
+            ConvRows<AT> rk[NKK], rq[NKK], rv[NKK];
+            wload();
+            fetch(1, rk);
+            fetch(0, rq);
+            fetch(2, rv);
+            wstore();
+            lds_barrier();                   // the staged weights
+            eval(1, rk, kk8);
+            eval(0, rq, kq);
+            eval(2, rv, kv);
+        } else {
+            // fp32 rows take twice the registers: one part ahead.
+            ConvRows<AT> ra[NKK], rb[NKK];
+            wload();
+            fetch(1, ra);
+            fetch(0, rb);
+            wstore();
+            lds_barrier();                   // the staged weights
+            eval(1, ra, kk8);
+            fetch(2, ra);
+            eval(0, rb, kq);
+            eval(2, ra, kv);
+        }
     } else {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -826,6 +910,43 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
             const int row = idx / ((BTP - BT) / 4), c4 = idx % ((BTP - BT) / 4);
             *reinterpret_cast<bf16x4*>(wU + frag<BTP>(row, BT + 4 * c4)) = bf16x4{};
         }
+
+    if constexpr (CONV) {
+        // The sequence's new conv state, this head's channels of q, k and v:
+        // its last W - 1 inputs (for a sequence shorter than that, the newest
+        // rows of the old state before them).  The sequence's first chunk
+        // writes it: that workgroup is the only reader of the old rows, and
+        // its reads completed before the conv evaluation.  Each thread reads
+        // all rows of its channels before writing any (the rows shift in
+        // place when the sequence is short).  In the fused front end q is the
+        // packed projection x (k and v are q + H d and q + 2 H d, one stride).
+        const int cslot = slots[seq];
+        if (x == first && cv.state && cslot < cv.num_slots) {
+            const int W = cv.width;
+            const int64_t hd = (int64_t)heads * D;
+            const int64_t s0 = cu[seq], s1 = cu[seq + 1];
+            const bool cinit = cv.has_init ? cv.has_init[seq] != 0 : true;
+            AT* stw = cv.state + (int64_t)cslot * (W - 1) * cv.channels;
+            constexpr int kG = D / 8;                      // 8-channel groups per part
+            for (int e = tid; e < 3 * kG; e += kThreads) {
+                const int part = e / kG;
+                const int64_t ch = part * hd + (int64_t)h * D + 8 * (e - part * kG);
+                Raw8<AT> rows[kMaxConvWidth - 1];
+#pragma unroll
+                for (int j = 0; j < kMaxConvWidth - 1; ++j) {
+                    if (j < W - 1) {
+                        const int64_t p = s1 - (W - 1) + j;
+                        rows[j] = p >= s0 ? load_raw8(q + p * qs + ch)
+                                : cinit   ? load_raw8(stw + (int64_t)((W - 1) - (s0 - p)) * cv.channels + ch)
+                                          : zero_raw8<AT>();
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kMaxConvWidth - 1; ++j)
+                    if (j < W - 1) store_raw8(stw + (int64_t)j * cv.channels + ch, rows[j]);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1246,7 +1367,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         ConvIn<AT> cv;
         cv.w = static_cast<const AT*>(a.conv_w);
         cv.b = static_cast<const AT*>(a.conv_b);
-        cv.state = static_cast<const AT*>(a.conv_state);
+        cv.state = static_cast<AT*>(a.conv_state);
         cv.has_init = a.has_init;
         cv.num_slots = a.num_slots;
         cv.channels = 3 * (int64_t)a.heads * D;
@@ -1267,19 +1388,6 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                                static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags, cv);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (a.conv_width > 0) {
-            // The conv state's new rows, once the intra kernel has read the old ones.
-            ConvArgs c;
-            c.x = a.q; c.x_stride = a.q_stride;
-            c.weight = a.conv_w; c.bias = a.conv_b;
-            c.state = a.conv_state; c.num_slots = a.num_slots;
-            c.cu_seqlens = a.cu_seqlens; c.slots = a.slots; c.has_init = a.has_init;
-            c.num_seqs = a.num_seqs; c.total_tokens = a.total_tokens;
-            c.channels = (int32_t)cv.channels; c.width = a.conv_width; c.flags = a.conv_flags;
-            c.y = nullptr; c.y_stride = 0; c.dtype = a.act;
-            e = launch_conv_state_update(c, stream);
-            if (e != hipSuccess) return e;
-        }
     }
     if (a.ev[1]) {
         const hipError_t e = hipEventRecord(a.ev[1], stream);
