@@ -45,8 +45,8 @@ MEASURED_TRAFFIC = {
               88383488, 73925120),
     "chain": (_PREFILL_SRC, "3085f456663abd88188dfbaf71e7f3ffbb540a2dd3d39d599750fbe4e234fe86",
               125572915, 68166963),
-    "decode": (_DECODE_SRC, "fa7de6ad27a89ac1caa9e5cea396351bd819ce2d5889c4a9d6de2cbff7eb9a57",
-               548016128, 539395994),
+    "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
+               547998632, 539231027),
 }
 
 
