@@ -335,30 +335,52 @@ kda_status_t kda_spec_commit(
     return launch_status(kda::launch_spec_commit(a, static_cast<hipStream_t>(stream)));
 }
 
-kda_status_t kda_gated_rmsnorm(
+kda_status_t kda_gated_rmsnorm_ex(
     const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
-    const void* weight, void* y, int64_t y_stride_t, kda_dtype_t dtype,
-    int64_t tokens, int32_t heads, int32_t dim, float eps, void* stream)
+    const void* residual, int64_t residual_stride_t, const void* weight, const void* bias,
+    void* y, int64_t y_stride_t, void* residual_out, int64_t residual_out_stride_t,
+    kda_dtype_t dtype, int64_t tokens, int32_t heads, int32_t dim, float eps, uint32_t flags,
+    void* stream)
 {
     if (tokens < 0 || heads <= 0 || !(eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
-    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16 && dtype != KDA_F16) return KDA_ERR_INVALID_ARG;
+    if (flags & ~(KDA_NORM_SIGMOID | KDA_NORM_RESIDUAL_F32)) return KDA_ERR_INVALID_ARG;
     if (dim <= 0 || dim > 1024 || dim % 8 != 0) return KDA_ERR_UNSUPPORTED;
     if (tokens == 0) return KDA_OK;
     if (!x || !gate || !y) return KDA_ERR_INVALID_ARG;
     const int64_t hd = (int64_t)heads * dim;
     if (x_stride_t < hd || gate_stride_t < hd || y_stride_t < hd) return KDA_ERR_INVALID_ARG;
-    if ((x_stride_t | gate_stride_t | y_stride_t) & 7) return KDA_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(gate) || !aligned16(y) || !aligned16(weight))
+    if (residual && residual_stride_t < hd) return KDA_ERR_INVALID_ARG;
+    if (residual_out && residual_out_stride_t < hd) return KDA_ERR_INVALID_ARG;
+    if ((x_stride_t | gate_stride_t | y_stride_t | (residual ? residual_stride_t : 0) |
+         (residual_out ? residual_out_stride_t : 0)) & 7)
+        return KDA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(gate) || !aligned16(y) || !aligned16(weight) ||
+        !aligned16(bias) || !aligned16(residual) || !aligned16(residual_out))
         return KDA_ERR_INVALID_ARG;
 
     kda::RmsNormArgs a;
     a.x = x; a.x_stride = x_stride_t;
     a.gate = gate; a.gate_stride = gate_stride_t;
-    a.weight = weight;
+    a.residual = residual; a.residual_stride = residual_stride_t;
+    a.weight = weight; a.bias = bias;
     a.y = y; a.y_stride = y_stride_t;
+    a.residual_out = residual_out; a.residual_out_stride = residual_out_stride_t;
     a.tokens = tokens; a.heads = heads; a.dim = dim;
     a.eps = eps; a.dtype = dtype;
+    a.sigmoid = (flags & KDA_NORM_SIGMOID) != 0;
+    a.residual_f32 = dtype == KDA_F32 || (flags & KDA_NORM_RESIDUAL_F32) != 0;
     return launch_status(kda::launch_gated_rmsnorm(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_gated_rmsnorm(
+    const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
+    const void* weight, void* y, int64_t y_stride_t, kda_dtype_t dtype,
+    int64_t tokens, int32_t heads, int32_t dim, float eps, void* stream)
+{
+    return kda_gated_rmsnorm_ex(x, x_stride_t, gate, gate_stride_t, nullptr, 0, weight, nullptr,
+                                y, y_stride_t, nullptr, 0, dtype, tokens, heads, dim, eps, 0u,
+                                stream);
 }
 
 kda_status_t kda_causal_conv1d(

@@ -68,11 +68,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 struct RmsNormArgs {
     const void* x; int64_t x_stride;
     const void* gate; int64_t gate_stride;
-    const void* weight;
+    const void* residual; int64_t residual_stride;      // null: no residual
+    const void* weight; const void* bias;               // null: 1 / 0
     void* y; int64_t y_stride;
+    void* residual_out; int64_t residual_out_stride;    // null: not written
     int64_t tokens; int32_t heads, dim;
     float eps;
     kda_dtype_t dtype;
+    bool sigmoid;                                       // gate activation sigmoid (else SiLU)
+    bool residual_f32;                                  // residual and residual_out in fp32
 };
 hipError_t launch_gated_rmsnorm(const RmsNormArgs& a, hipStream_t stream);
 

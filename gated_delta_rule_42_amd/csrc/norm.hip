@@ -2,21 +2,29 @@
 //
 // Page "[Feature][KDA] Add Kimi K3 KDA execution", What this PR does: the KDA
 // output goes through a fused normalisation-and-gating step whose result is
-// allocated separately so the input is preserved; the gate may be a packed
-// (strided) tensor.
+// allocated separately so the input is preserved; How was this patch tested:
+// the norm-gate variants are fp16 and bf16 data, sigmoid and SiLU gates,
+// packed (strided) gates, the affine path, and the residual / prenorm path.
 //
-//     y = x * rsqrt(mean(x^2) + eps) * w * silu(gate)
+//     h = x + residual                        (residual optional, fp32 sum)
+//     residual_out = h                        (optional: the prenorm output)
+//     y = (h * rsqrt(mean(h^2) + eps) * w + b) * act(gate)
+//     act(z) = z * sigmoid(z)  (SiLU)  or  sigmoid(z)
 //
-// HBM-bound (reads x and gate once, writes y once).  LPR lanes share one row:
-// each lane owns dim/LPR elements in 8-element vectors (16 B for bf16), the
-// sum of squares is reduced across the LPR lanes with shuffles in a fixed
-// order, so results are deterministic.
+// HBM-bound (reads x, residual and gate once, writes y and residual_out
+// once).  LPR lanes share one row: each lane owns dim/LPR elements in
+// 8-element vectors, the sum of squares is reduced across the LPR lanes with
+// shuffles in a fixed order, so results are deterministic.  x (and the
+// residual) are read a second time after the reduction, from the cache.
 
 #include "kda_device.cuh"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void load8(const float* p, float (&x)[8])
 {
@@ -28,6 +36,12 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8])
 __device__ __forceinline__ void load8(const bf16* p, float (&x)[8])
 {
     const bf16x8 t = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(t[i]);
+}
+__device__ __forceinline__ void load8(const f16* p, float (&x)[8])
+{
+    const f16x8 t = *reinterpret_cast<const f16x8*>(p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(t[i]);
 }
@@ -43,43 +57,72 @@ __device__ __forceinline__ void store8(bf16* p, const float (&x)[8])
     for (int i = 0; i < 8; ++i) t[i] = static_cast<bf16>(x[i]);
     *reinterpret_cast<bf16x8*>(p) = t;
 }
+__device__ __forceinline__ void store8(f16* p, const float (&x)[8])
+{
+    f16x8 t;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = static_cast<f16>(x[i]);
+    *reinterpret_cast<f16x8*>(p) = t;
+}
 
 constexpr int kNormBlock = 256;
 
-template <int LPR, typename T>
+// T: x, gate, weight, bias and y; R: residual and residual_out (T or fp32).
+// PLAIN: no residual, no residual_out, no bias and the SiLU gate, known at
+// compile time (the kernel is bound by its vector instructions about as much
+// as by HBM, so the plain norm of the KDA output gets its own copy).
+template <int LPR, bool PLAIN, typename T, typename R>
 __global__ __launch_bounds__(kNormBlock)
 void gated_rmsnorm_kernel(const T* __restrict__ x, int64_t xs, const T* __restrict__ gate,
-                          int64_t gs, const T* __restrict__ w, T* __restrict__ y, int64_t ys,
-                          int64_t rows, int heads, int dim, float eps)
+                          int64_t gs, const R* __restrict__ res, int64_t rs,
+                          const T* __restrict__ w, const T* __restrict__ bias,
+                          T* __restrict__ y, int64_t ys, R* __restrict__ res_out, int64_t ros,
+                          int64_t rows, int heads, int dim, float eps, bool sigmoid)
 {
     constexpr int kRowsPerBlock = kNormBlock / LPR;
     const int lane_in_row = threadIdx.x % LPR;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / LPR;
     const bool live = row < rows;
     const int64_t t = live ? row / heads : 0;
-    const int h = live ? (int)(row % heads) : 0;
-    const T* xr = x + t * xs + (int64_t)h * dim;
-    const T* gr = gate + t * gs + (int64_t)h * dim;
-    T* yr = y + t * ys + (int64_t)h * dim;
+    const int64_t off = live ? (int64_t)(row % heads) * dim : 0;
+    const T* xr = x + t * xs + off;
+    const T* gr = gate + t * gs + off;
+    const R* rr = !PLAIN && res ? res + t * rs + off : nullptr;
+    R* ror = !PLAIN && res_out ? res_out + t * ros + off : nullptr;
+    const T* bb = PLAIN ? nullptr : bias;
+    const bool sig = !PLAIN && sigmoid;
+    T* yr = y + t * ys + off;
 
-    // Sum of squares over the row (each lane: its 8-element vectors).
+    // h = x (+ residual) for one of this lane's vectors.
+    auto row_vec = [&](int c, float (&hv)[8]) {
+        load8(xr + c, hv);
+        if (rr) {
+            float rv[8];
+            load8(rr + c, rv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hv[i] += rv[i];
+        }
+    };
+
+    // Sum of squares of h; the prenorm output is written here.
     float ss = 0.0f;
     if (live) {
         for (int c = lane_in_row * 8; c < dim; c += LPR * 8) {
-            float xv[8];
-            load8(xr + c, xv);
+            float hv[8];
+            row_vec(c, hv);
+            if (ror) store8(ror + c, hv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss += xv[i] * xv[i];
+            for (int i = 0; i < 8; ++i) ss += hv[i] * hv[i];
         }
     }
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, LPR);
+    for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, LPR);
     if (!live) return;
     const float inv = 1.0f / sqrtf(ss / (float)dim + eps);
 
     for (int c = lane_in_row * 8; c < dim; c += LPR * 8) {
-        float xv[8], gv[8], wv[8], out[8];
-        load8(xr + c, xv);
+        float hv[8], gv[8], wv[8], bv[8], out[8];
+        row_vec(c, hv);
         load8(gr + c, gv);
         if (w) {
             load8(w + c, wv);
@@ -87,32 +130,42 @@ void gated_rmsnorm_kernel(const T* __restrict__ x, int64_t xs, const T* __restri
 #pragma unroll
             for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
         }
+        if (bb) {
+            load8(bb + c, bv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bv[i] = 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            // sigmoid(z) with the hardware reciprocal (within 1 ulp).
             const float z = gv[i];
-            const float silu = z / (1.0f + __expf(-z));
-            out[i] = xv[i] * inv * wv[i] * silu;
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+            const float act = sig ? sg : z * sg;
+            out[i] = (hv[i] * inv * wv[i] + bv[i]) * act;
         }
         store8(yr + c, out);
     }
 }
 
-template <int LPR, typename T>
+template <int LPR, bool PLAIN, typename T, typename R>
 hipError_t launch_lpr(const RmsNormArgs& a, hipStream_t stream)
 {
     const int64_t rows = a.tokens * a.heads;
     constexpr int kRowsPerBlock = kNormBlock / LPR;
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gated_rmsnorm_kernel<LPR, T>), dim3((unsigned)blocks), dim3(kNormBlock),
-                       0, stream, static_cast<const T*>(a.x), a.x_stride,
+    hipLaunchKernelGGL((gated_rmsnorm_kernel<LPR, PLAIN, T, R>), dim3((unsigned)blocks),
+                       dim3(kNormBlock), 0, stream, static_cast<const T*>(a.x), a.x_stride,
                        static_cast<const T*>(a.gate), a.gate_stride,
-                       static_cast<const T*>(a.weight), static_cast<T*>(a.y), a.y_stride, rows,
-                       a.heads, a.dim, a.eps);
+                       static_cast<const R*>(a.residual), a.residual_stride,
+                       static_cast<const T*>(a.weight), static_cast<const T*>(a.bias),
+                       static_cast<T*>(a.y), a.y_stride, static_cast<R*>(a.residual_out),
+                       a.residual_out_stride, rows, a.heads, a.dim, a.eps, a.sigmoid);
     return hipGetLastError();
 }
 
-template <typename T>
+template <bool PLAIN, typename T, typename R>
 hipError_t launch_typed(const RmsNormArgs& a, hipStream_t stream)
 {
     // Largest power-of-two lane count (<= 64) that splits the row into whole
@@ -121,21 +174,34 @@ hipError_t launch_typed(const RmsNormArgs& a, hipStream_t stream)
     int lpr = 64;
     while (lpr > 1 && vecs % lpr != 0) lpr >>= 1;
     switch (lpr) {
-        case 64: return launch_lpr<64, T>(a, stream);
-        case 32: return launch_lpr<32, T>(a, stream);
-        case 16: return launch_lpr<16, T>(a, stream);
-        case 8: return launch_lpr<8, T>(a, stream);
-        case 4: return launch_lpr<4, T>(a, stream);
-        case 2: return launch_lpr<2, T>(a, stream);
-        default: return launch_lpr<1, T>(a, stream);
+        case 64: return launch_lpr<64, PLAIN, T, R>(a, stream);
+        case 32: return launch_lpr<32, PLAIN, T, R>(a, stream);
+        case 16: return launch_lpr<16, PLAIN, T, R>(a, stream);
+        case 8: return launch_lpr<8, PLAIN, T, R>(a, stream);
+        case 4: return launch_lpr<4, PLAIN, T, R>(a, stream);
+        case 2: return launch_lpr<2, PLAIN, T, R>(a, stream);
+        default: return launch_lpr<1, PLAIN, T, R>(a, stream);
     }
+}
+
+template <typename T>
+hipError_t launch_variant(const RmsNormArgs& a, hipStream_t stream)
+{
+    if (!a.residual && !a.residual_out && !a.bias && !a.sigmoid)
+        return launch_typed<true, T, T>(a, stream);
+    if (a.residual_f32) return launch_typed<false, T, float>(a, stream);
+    return launch_typed<false, T, T>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gated_rmsnorm(const RmsNormArgs& a, hipStream_t stream)
 {
-    return a.dtype == KDA_BF16 ? launch_typed<bf16>(a, stream) : launch_typed<float>(a, stream);
+    switch (a.dtype) {
+        case KDA_BF16: return launch_variant<bf16>(a, stream);
+        case KDA_F16: return launch_variant<f16>(a, stream);
+        default: return launch_variant<float>(a, stream);
+    }
 }
 
 }  // namespace kda

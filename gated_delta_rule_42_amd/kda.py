@@ -23,10 +23,13 @@ KDA_ERR_LAUNCH = 4
 
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_F16 = 2
 KDA_FLAG_QK_L2NORM = 1
 KDA_CONV_SILU = 1
+KDA_NORM_SIGMOID = 1
+KDA_NORM_RESIDUAL_F32 = 2
 
-_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16, torch.float16: KDA_F16}
 
 
 class KdaError(RuntimeError):
@@ -68,6 +71,9 @@ def _load() -> ctypes.CDLL:
         vp, i32, i64, vp, f32, u32, vp, i64, vp]
     lib.kda_gated_rmsnorm.restype = i32
     lib.kda_gated_rmsnorm.argtypes = [vp, i64, vp, i64, vp, vp, i64, i32, i64, i32, i32, f32, vp]
+    lib.kda_gated_rmsnorm_ex.restype = i32
+    lib.kda_gated_rmsnorm_ex.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, vp, i64,
+                                         i32, i64, i32, i32, f32, u32, vp]
     lib.kda_causal_conv1d.restype = i32
     lib.kda_causal_conv1d.argtypes = [
         vp, i64, vp, vp, vp, i64, vp, vp, vp, i32, i64, i32, i32, i32, u32, vp, i64, vp]
@@ -307,6 +313,32 @@ def gated_rmsnorm(x, gate, y, *, weight=None, eps: float = 1e-6, stream=None) ->
         _ptr(weight), _ptr(y), _token_stride(y, "y"), _dtype(x), T, H, dim, float(eps),
         _stream(stream))
     _check("kda_gated_rmsnorm", status)
+
+
+def gated_rmsnorm_ex(x, gate, y, *, residual=None, residual_out=None, weight=None, bias=None,
+                     activation: str = "silu", eps: float = 1e-6, stream=None) -> None:
+    """kda_gated_rmsnorm_ex on [T,H,dim] (token-strided views allowed).
+    residual / residual_out: x's dtype, or both fp32 (KDA_NORM_RESIDUAL_F32);
+    activation "silu" or "sigmoid"."""
+    T, H, dim = x.shape
+    if activation not in ("silu", "sigmoid"):
+        raise ValueError("activation must be 'silu' or 'sigmoid'")
+    for t, name in ((weight, "weight"), (bias, "bias")):
+        if t is not None:
+            _contig(t, name, x.dtype)
+    rdt = {t.dtype for t in (residual, residual_out) if t is not None}
+    if len(rdt) > 1 or (rdt and rdt != {x.dtype} and rdt != {torch.float32}):
+        raise ValueError("residual and residual_out must share x's dtype or be fp32")
+    flags = KDA_NORM_SIGMOID if activation == "sigmoid" else 0
+    if rdt == {torch.float32}:
+        flags |= KDA_NORM_RESIDUAL_F32
+    status = _lib.kda_gated_rmsnorm_ex(
+        _ptr(x), _token_stride(x, "x"), _ptr(gate), _token_stride(gate, "gate"),
+        _ptr(residual), 0 if residual is None else _token_stride(residual, "residual"),
+        _ptr(weight), _ptr(bias), _ptr(y), _token_stride(y, "y"),
+        _ptr(residual_out), 0 if residual_out is None else _token_stride(residual_out, "residual_out"),
+        _dtype(x), T, H, dim, float(eps), flags, _stream(stream))
+    _check("kda_gated_rmsnorm_ex", status)
 
 
 def causal_conv1d(x, weight, cu_seqlens, conv_state_pool, state_indices, y, *, bias=None,

@@ -62,10 +62,13 @@ typedef int32_t kda_status_t;
 typedef int32_t kda_dtype_t;
 #define KDA_F32 0
 #define KDA_BF16 1
+#define KDA_F16 2      /* IEEE half: the gated RMSNorm entry points only */
 
 /* Flags. */
 #define KDA_FLAG_QK_L2NORM 1u   /* q, k <- x / sqrt(sum x^2 + 1e-6) per (token, head) in-kernel */
 #define KDA_CONV_SILU 1u        /* apply SiLU after the convolution                        */
+#define KDA_NORM_SIGMOID 1u      /* gated norm: gate activation sigmoid(z), not z*sigmoid(z) */
+#define KDA_NORM_RESIDUAL_F32 2u /* gated norm: residual and residual_out are fp32            */
 
 /* Supported shapes: d_k = d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64}. */
 
@@ -183,12 +186,40 @@ kda_status_t kda_recurrent_decode(
  * statistics over the `dim` elements of one (token, head).  x, gate, y have
  * per-token strides (elements) so packed gates can be read in place; heads
  * of one token are contiguous blocks of `dim`.  weight is [dim] of `dtype` or
- * NULL (no affine).  Math in fp32; y may not alias x or gate.
+ * NULL (no affine).  dtype KDA_F32, KDA_BF16 or KDA_F16.  Math in fp32; y may
+ * not alias x or gate.
  */
 kda_status_t kda_gated_rmsnorm(
     const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
     const void* weight, void* y, int64_t y_stride_t, kda_dtype_t dtype,
     int64_t tokens, int32_t heads, int32_t dim, float eps, void* stream);
+
+/*
+ * Gated RMSNorm variants (page "Add Kimi K3 KDA execution", How was this
+ * patch tested: the norm-gate cases cover fp16 and bf16 data, sigmoid and SiLU
+ * gates, packed gate strides, the affine path, the residual / prenorm path,
+ * and preserving the input):
+ *
+ *     h = x + residual                       (residual NULL: h = x)
+ *     residual_out = h                       (residual_out NULL: not written)
+ *     y = (h / sqrt(mean(h^2) + eps) * weight + bias) * act(gate)
+ *     act(z) = z*sigmoid(z), or sigmoid(z) with KDA_NORM_SIGMOID
+ *
+ * The sum h is formed in fp32; the norm uses that unrounded sum, and
+ * residual_out stores it rounded to its type.  x, gate, y, weight [dim] and
+ * bias [dim] (either may be NULL) are of `dtype` (KDA_F32, KDA_BF16 or
+ * KDA_F16); residual and residual_out are of `dtype` too, or fp32 with
+ * KDA_NORM_RESIDUAL_F32 (always fp32 when dtype is KDA_F32).  Strides are per
+ * token, in elements, multiples of 8; every pointer 16-byte aligned.  No
+ * output may alias an input.  kda_gated_rmsnorm is this call with no
+ * residual, no bias and the SiLU gate.
+ */
+kda_status_t kda_gated_rmsnorm_ex(
+    const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
+    const void* residual, int64_t residual_stride_t, const void* weight, const void* bias,
+    void* y, int64_t y_stride_t, void* residual_out, int64_t residual_out_stride_t,
+    kda_dtype_t dtype, int64_t tokens, int32_t heads, int32_t dim, float eps, uint32_t flags,
+    void* stream);
 
 /*
  * Causal depthwise conv1d over a varlen token batch with a rolling per-slot

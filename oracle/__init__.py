@@ -13,6 +13,7 @@ Functions (all return new arrays; inputs are never modified):
   spec_commit(...)  accept a prefix: copy its last state into the pool (kda_oracle.c)
   conv1d(...)       causal depthwise conv1d with rolling conv state    (kda_oracle.c)
   gated_rmsnorm(...) RMSNorm then SiLU gate                           (kda_oracle.c)
+  gated_rmsnorm_ex(...) with residual (prenorm sum), bias, sigmoid gate (kda_oracle.c)
   chunk_form.*      the chunked algebra in fp64, a second algorithm used to pin
                     the token loop (see chunk_form.py)
 
@@ -91,6 +92,10 @@ class Oracle:
         lib.kda_oracle_gated_rmsnorm.restype = ctypes.c_int
         lib.kda_oracle_gated_rmsnorm.argtypes = [
             _f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _f64p]
+        lib.kda_oracle_gated_rmsnorm_ex.restype = ctypes.c_int
+        lib.kda_oracle_gated_rmsnorm_ex.argtypes = [
+            _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int, _f64p, _f64p]
         self.lib = lib
 
     def num_threads(self) -> int:
@@ -224,6 +229,26 @@ class Oracle:
             raise ValueError(f"kda_oracle_gated_rmsnorm failed with status {rc}")
         return y.reshape(shape)
 
+    def gated_rmsnorm_ex(self, x, gate, w=None, b=None, eps: float = 1e-6, *, residual=None,
+                         sigmoid: bool = False):
+        """x, gate, residual [..., dim]; w, b [dim] or None.  Returns (y, h) with
+        h = x + residual (x when residual is None), both with x's shape."""
+        x, gate = _f64(x), _f64(gate)
+        shape = x.shape
+        dim = shape[-1]
+        x2, g2 = x.reshape(-1, dim), gate.reshape(-1, dim)
+        r2 = None if residual is None else _f64(residual).reshape(-1, dim)
+        ww = None if w is None else _f64(w)
+        bb = None if b is None else _f64(b)
+        y = np.full_like(x2, np.nan)
+        h = np.full_like(x2, np.nan)
+        rc = self.lib.kda_oracle_gated_rmsnorm_ex(
+            _ptr(x2, _f64p), _ptr(g2, _f64p), _ptr(r2, _f64p), _ptr(ww, _f64p), _ptr(bb, _f64p),
+            x2.shape[0], dim, float(eps), int(bool(sigmoid)), _ptr(y, _f64p), _ptr(h, _f64p))
+        if rc != 0:
+            raise ValueError(f"kda_oracle_gated_rmsnorm_ex failed with status {rc}")
+        return y.reshape(shape), h.reshape(shape)
+
 
 _DEFAULT: Oracle | None = None
 
@@ -261,6 +286,10 @@ def conv1d(*args, **kwargs):
 
 def gated_rmsnorm(*args, **kwargs):
     return default().gated_rmsnorm(*args, **kwargs)
+
+
+def gated_rmsnorm_ex(*args, **kwargs):
+    return default().gated_rmsnorm_ex(*args, **kwargs)
 
 
 def num_threads() -> int:

@@ -389,26 +389,42 @@ int kda_oracle_conv1d(const double* x, const double* w, const double* bias,
 /*
  * Gated RMSNorm, norm before gate (page "Add Kimi K3 KDA execution", What this
  * PR does: output normalisation and gating, result in a separate buffer so
- * the input is preserved):
- *   y = x / sqrt(mean(x^2) + eps) * w * silu(gate),  silu(z) = z / (1 + e^-z)
- * per row of `dim` elements; w is [dim] or NULL (no affine weight).
+ * the input is preserved; How was this patch tested: sigmoid and SiLU gates,
+ * the affine path and the residual / prenorm path).  Per row of `dim`:
+ *   h = x + residual                     (residual NULL: h = x)
+ *   h_out = h                            (h_out NULL: not written)
+ *   y = (h / sqrt(mean(h^2) + eps) * w + b) * act(gate)
+ *   act(z) = z / (1 + e^-z)  (SiLU),  or  1 / (1 + e^-z) when `sigmoid`
+ * w and b are [dim] or NULL (weight 1, bias 0).
  */
-int kda_oracle_gated_rmsnorm(const double* x, const double* gate, const double* w,
-                             int64_t rows, int64_t dim, double eps, double* y)
+int kda_oracle_gated_rmsnorm_ex(const double* x, const double* gate, const double* residual,
+                                const double* w, const double* b, int64_t rows, int64_t dim,
+                                double eps, int sigmoid, double* y, double* h_out)
 {
     if (rows < 0 || dim <= 0) return ORACLE_EINVAL;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-        const double* xr = x + r * dim;
+        double* h = (double*)malloc((size_t)dim * sizeof(double));
         const double* gr = gate + r * dim;
+        for (int64_t c = 0; c < dim; ++c)
+            h[c] = x[r * dim + c] + (residual ? residual[r * dim + c] : 0.0);
+        if (h_out) memcpy(h_out + r * dim, h, (size_t)dim * sizeof(double));
         double ss = 0.0;
-        for (int64_t c = 0; c < dim; ++c) ss += xr[c] * xr[c];
+        for (int64_t c = 0; c < dim; ++c) ss += h[c] * h[c];
         double inv = 1.0 / sqrt(ss / (double)dim + eps);
         for (int64_t c = 0; c < dim; ++c) {
             double z = gr[c];
-            double act = z / (1.0 + exp(-z));
-            y[r * dim + c] = xr[c] * inv * (w ? w[c] : 1.0) * act;
+            double act = sigmoid ? 1.0 / (1.0 + exp(-z)) : z / (1.0 + exp(-z));
+            y[r * dim + c] = (h[c] * inv * (w ? w[c] : 1.0) + (b ? b[c] : 0.0)) * act;
         }
+        free(h);
     }
     return ORACLE_OK;
+}
+
+/* The plain gated RMSNorm: no residual, no bias, SiLU gate. */
+int kda_oracle_gated_rmsnorm(const double* x, const double* gate, const double* w,
+                             int64_t rows, int64_t dim, double eps, double* y)
+{
+    return kda_oracle_gated_rmsnorm_ex(x, gate, NULL, w, NULL, rows, dim, eps, 0, y, NULL);
 }

@@ -141,7 +141,7 @@ def oracle_decode(case: wl.DecodeCase, pool=None):
 
 
 def bits(t: torch.Tensor) -> torch.Tensor:
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
 def inv_sqrt(d: int) -> float:

@@ -23,6 +23,7 @@ algorithm):
   conv_numpy         conv1d equals numpy.convolve per channel, SiLU from scipy
   conv_state         conv1d state carries across split calls
   rmsnorm_library    gated RMSNorm equals torch rms_norm times silu (float64)
+  rmsnorm_variants   residual/prenorm, bias and sigmoid gate vs torch (float64)
 """
 from __future__ import annotations
 
@@ -327,6 +328,35 @@ def pin_rmsnorm_library(orc):
            1e-14, "constant rows: c / sqrt(c^2 + eps) * silu(gate)")
 
 
+def pin_rmsnorm_variants(orc):
+    """Residual / prenorm, bias and the sigmoid gate against torch's rms_norm,
+    sigmoid and silu in float64; y_silu = y_sigmoid * gate; with weight 0 the
+    output is bias * act(gate)."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(115)
+    rows, dim, eps = 9, 24, 1e-6
+    x, gate, res = (rng.standard_normal((rows, dim)) for _ in range(3))
+    w = 1.0 + 0.1 * rng.standard_normal(dim)
+    b = 0.3 * rng.standard_normal(dim)
+    gt = torch.from_numpy(gate)
+    hsum = x + res
+    normed = (F.rms_norm(torch.from_numpy(hsum), (dim,), torch.from_numpy(w), eps)
+              + torch.from_numpy(b))
+    for sig, act in ((False, F.silu(gt)), (True, torch.sigmoid(gt))):
+        y, h = orc.gated_rmsnorm_ex(x, gate, w, b, eps, residual=res, sigmoid=sig)
+        _close(y, (normed * act).numpy(), 1e-13, f"gated RMSNorm variant sigmoid={sig}")
+        _close(h, hsum, 0.0, "prenorm output h = x + residual")
+    y_silu, _ = orc.gated_rmsnorm_ex(x, gate, w, b, eps, residual=res)
+    y_sig, _ = orc.gated_rmsnorm_ex(x, gate, w, b, eps, residual=res, sigmoid=True)
+    _close(y_silu, y_sig * gate, 1e-13, "silu gate = sigmoid gate times gate")
+    y0, h0 = orc.gated_rmsnorm_ex(x, gate, np.zeros(dim), b, eps)
+    _close(y0, b * (F.silu(gt)).numpy(), 1e-14, "weight 0: bias * act(gate)")
+    _close(h0, x, 0.0, "no residual: h = x")
+    y1, _ = orc.gated_rmsnorm_ex(x, gate, w, None, eps)
+    _close(y1, orc.gated_rmsnorm(x, gate, w, eps), 0.0, "no residual, no bias = plain norm")
+
+
 def pin_spec_decode(orc):
     """Speculative decode: row b's ntok tokens from pool[slot_b], state after
     each token, pool untouched; commit copies an accepted prefix's state."""
@@ -371,4 +401,4 @@ def pin_spec_decode(orc):
 ALL_PINS = [pin_hand_worked, pin_beta_zero, pin_exact_retrieval, pin_delta_invariant,
             pin_linearity, pin_chunk_form, pin_split_calls, pin_checkpoints, pin_decode,
             pin_padding_empty, pin_has_init, pin_l2norm, pin_conv_numpy, pin_conv_state,
-            pin_rmsnorm_library, pin_spec_decode]
+            pin_rmsnorm_library, pin_rmsnorm_variants, pin_spec_decode]

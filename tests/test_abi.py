@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_chunk_prefill", "kda_recurrent_decode", "kda_gated_rmsnorm",
                  "kda_causal_conv1d", "kda_chunk_prefill_workspace_size",
-                 "kda_conv_chunk_prefill", "kda_spec_decode", "kda_spec_commit",
+                 "kda_conv_chunk_prefill", "kda_gated_rmsnorm_ex", "kda_spec_decode", "kda_spec_commit",
                  "kda_abi_version", "kda_status_string"):
         assert want in names
 
@@ -203,6 +203,20 @@ def test_norm_and_conv_validation(lib):
     assert n(gate=None) == K.KDA_ERR_INVALID_ARG
     assert n(eps=-1.0) == K.KDA_ERR_INVALID_ARG
     assert n(ys=1000) == K.KDA_ERR_INVALID_ARG
+    nx = lambda **o: lib.kda_gated_rmsnorm_ex(*dict(
+        dict(x=FAKE, xs=2048, gate=FAKE, gs=2048, r=None, rs=0, w=None, b=None, y=FAKE, ys=2048,
+             ro=None, ros=0, dt=2, T=4, H=16, dim=128, eps=1e-6, flags=0, stream=None),
+        **o).values())
+    assert nx(T=0) == K.KDA_OK
+    assert nx(dt=3) == K.KDA_ERR_INVALID_ARG
+    assert nx(flags=4) == K.KDA_ERR_INVALID_ARG
+    assert nx(dim=12) == K.KDA_ERR_UNSUPPORTED
+    assert nx(r=FAKE, rs=100) == K.KDA_ERR_INVALID_ARG        # residual stride < H * dim
+    assert nx(ro=FAKE, ros=2052) == K.KDA_ERR_INVALID_ARG     # not a multiple of 8
+    assert nx(b=FAKE + 2) == K.KDA_ERR_INVALID_ARG            # misaligned bias
+    assert nx(ro=FAKE + 8, ros=2048) == K.KDA_ERR_INVALID_ARG
+    # fp16 is a norm-only type: the attention entry points reject it.
+    assert _prefill(lib, act=2) == K.KDA_ERR_INVALID_ARG
     c = lambda **o: lib.kda_causal_conv1d(*dict(
         dict(x=FAKE, xs=6144, w=FAKE, b=None, st=FAKE, slots=4, cu=FAKE, idx=FAKE, hi=None,
              n=1, T=64, C=6144, W=4, dt=1, flags=1, y=FAKE, ys=6144, stream=None), **o).values())

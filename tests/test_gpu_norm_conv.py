@@ -8,15 +8,16 @@ from tests.gpu_support import bits, f64, max_err, say
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16 = torch.float32, torch.bfloat16
+F32, BF16, F16 = torch.float32, torch.bfloat16, torch.float16
 
 
 def _excess(got, ref, dtype) -> float:
     """Largest error beyond what rounding the output to `dtype` explains:
-    |got - ref| - 2^-8 |ref| for bf16 (RNE is within 2^-9 relative), the plain
-    error for fp32.  fp32 arithmetic leaves ~1e-6."""
+    |got - ref| - 2^-8 |ref| for bf16 (RNE is within 2^-9 relative), 2^-10 |ref|
+    for fp16 (within 2^-11), the plain error for fp32.  fp32 arithmetic leaves
+    ~1e-6."""
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
-    slack = 2.0 ** -8 * np.abs(ref) if dtype == BF16 else 0.0
+    slack = {BF16: 2.0 ** -8, F16: 2.0 ** -10}.get(dtype, 0.0) * np.abs(ref)
     return float(np.max(np.abs(got - ref) - slack)) if got.size else 0.0
 
 
@@ -58,6 +59,69 @@ def test_gated_rmsnorm_packed_gate():
     torch.cuda.synchronize()
     ref = oracle.gated_rmsnorm(f64(x), f64(gate.contiguous()), None, 1e-6)
     assert _excess(f64(y), ref, BF16) <= TOL_ABS
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16, F32])
+@pytest.mark.parametrize("activation", ["silu", "sigmoid"])
+@pytest.mark.parametrize("residual", [None, "same", "fp32"])
+def test_gated_rmsnorm_variants(dtype, activation, residual):
+    """kda_gated_rmsnorm_ex: fp16/bf16/fp32, SiLU or sigmoid gate, weight and
+    bias, a packed (strided) gate, residual in x's dtype or fp32 with the
+    prenorm sum written out; inputs preserved."""
+    from gated_delta_rule_42_amd import kda
+    if residual == "fp32" and dtype == F32:
+        pytest.skip("fp32 data already has an fp32 residual")
+    g = torch.Generator().manual_seed(17)
+    T, H, dim = 29, 3, 128
+    x = torch.randn(T, H, dim, generator=g).to(dtype)
+    packed = torch.randn(T, 3 * H * dim, generator=g).to(dtype)
+    gate_h = packed[:, H * dim:2 * H * dim].reshape(T, H, dim)
+    w = (1 + 0.1 * torch.randn(dim, generator=g)).to(dtype)
+    b = (0.2 * torch.randn(dim, generator=g)).to(dtype)
+    rdt = None if residual is None else (F32 if residual == "fp32" else dtype)
+    r = None if rdt is None else torch.randn(T, H, dim, generator=g).to(rdt)
+    xd, pd = x.cuda(), packed.cuda()
+    gd = pd[:, H * dim:2 * H * dim].view(T, H, dim)
+    rd = None if r is None else r.cuda()
+    y = torch.full_like(xd, float("nan"))
+    ro = torch.full((T, H, dim), float("nan"), dtype=rdt or dtype, device="cuda")
+    kda.gated_rmsnorm_ex(xd, gd, y, residual=rd, residual_out=ro, weight=w.cuda(), bias=b.cuda(),
+                         activation=activation, eps=1e-6)
+    torch.cuda.synchronize()
+    y_r, h_r = oracle.gated_rmsnorm_ex(f64(x), f64(gate_h), f64(w), f64(b), 1e-6,
+                                       residual=None if r is None else f64(r),
+                                       sigmoid=activation == "sigmoid")
+    e = _excess(f64(y), y_r, dtype)
+    say(f"  norm {dtype} {activation} residual={residual}: max abs {max_err(f64(y), y_r):.2e}, "
+        f"beyond output rounding {e:.2e}")
+    assert e <= TOL_ABS
+    # The prenorm output is the fp32 sum rounded to its type.
+    want = x.float() + (0 if r is None else r.float())
+    assert torch.equal(bits(ro.cpu()), bits(want.to(rdt or dtype))), "residual_out"
+    assert max_err(f64(ro), h_r) <= (0.0 if (rdt or dtype) == F32 and r is None else 2e-2)
+    assert torch.equal(bits(xd.cpu()), bits(x)) and torch.equal(bits(pd.cpu()), bits(packed))
+    if rd is not None:
+        assert torch.equal(bits(rd.cpu()), bits(r))
+
+
+@pytest.mark.parametrize("dim", [64, 96, 512, 1024, 8])
+def test_gated_rmsnorm_variants_dims_no_affine(dim):
+    """No weight, no bias, no residual_out, other row widths: equals the
+    plain kda_gated_rmsnorm bit for bit for the SiLU gate."""
+    from gated_delta_rule_42_amd import kda
+    g = torch.Generator().manual_seed(dim + 1)
+    T, H = 13, 2
+    x = torch.randn(T, H, dim, generator=g).to(F16).cuda()
+    gate = torch.randn(T, H, dim, generator=g).to(F16).cuda()
+    y1, y2 = torch.empty_like(x), torch.empty_like(x)
+    kda.gated_rmsnorm_ex(x, gate, y1)
+    kda.gated_rmsnorm(x, gate, y2)
+    y3 = torch.empty_like(x)
+    kda.gated_rmsnorm_ex(x, gate, y3, activation="sigmoid")
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y1.cpu()), bits(y2.cpu()))
+    ref, _ = oracle.gated_rmsnorm_ex(f64(x), f64(gate), None, None, 1e-6, sigmoid=True)
+    assert _excess(f64(y3), ref, F16) <= TOL_ABS
 
 
 def _conv_case(seed, lens, C, W, dtype, slots, has_init, bias):

@@ -71,8 +71,13 @@ MUTANTS = {
     "spec_commit_takes_last_draft": _sub("token_states + ((b * ntok + accepted[b] - 1) * H + h)",
                                          "token_states + ((b * ntok + ntok - 1) * H + h)"),
     "rmsnorm_sum_not_mean": _sub("ss / (double)dim + eps", "ss + eps"),
-    "rmsnorm_sigmoid_not_silu": _sub("double act = z / (1.0 + exp(-z));",
-                                     "double act = 1.0 / (1.0 + exp(-z));"),
+    "rmsnorm_sigmoid_not_silu": _sub(": z / (1.0 + exp(-z));", ": 1.0 / (1.0 + exp(-z));"),
+    "rmsnorm_silu_for_sigmoid": _sub("sigmoid ? 1.0 / (1.0 + exp(-z))", "sigmoid ? z / (1.0 + exp(-z))"),
+    "rmsnorm_residual_dropped": _sub("x[r * dim + c] + (residual ? residual[r * dim + c] : 0.0)",
+                                     "x[r * dim + c]"),
+    "rmsnorm_bias_after_gate": _sub(
+        "(h[c] * inv * (w ? w[c] : 1.0) + (b ? b[c] : 0.0)) * act",
+        "h[c] * inv * (w ? w[c] : 1.0) * act + (b ? b[c] : 0.0)"),
 }
 
 
