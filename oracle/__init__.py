@@ -68,6 +68,13 @@ class Oracle:
             _f64p, ctypes.c_int64, _i64p, _u8p,
             _f64p, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_double, _f64p]
+        lib.kda_oracle_prefill_at.restype = ctypes.c_int
+        lib.kda_oracle_prefill_at.argtypes = [
+            _f64p, _f64p, _f64p, _f64p, _f64p,
+            _i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _f64p, ctypes.c_int64, _i64p, _u8p, _i64p,
+            _f64p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, ctypes.c_double, _f64p]
         lib.kda_oracle_decode.restype = ctypes.c_int
         lib.kda_oracle_decode.argtypes = [
             _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int64,
@@ -103,9 +110,12 @@ class Oracle:
 
     def prefill(self, q, k, v, g, beta, cu_seqlens, pool, slots, has_init=None,
                 ckpt_interval: int = 0, ckpt_capacity: int | None = None,
-                scale: float = 1.0, l2norm_qk: bool = False, l2_eps: float = 1e-6):
+                scale: float = 1.0, l2norm_qk: bool = False, l2_eps: float = 1e-6,
+                start_pos=None):
         """Varlen prefill.  q,k,g [T,H,dk]; v [T,H,dv]; beta [T,H];
-        cu_seqlens [N+1]; pool [slots,H,dk,dv]; slots [N] (<0 = padding).
+        cu_seqlens [N+1]; pool [slots,H,dk,dv]; slots [N] (<0 = padding);
+        start_pos [N] or None: absolute position of each sequence's first
+        token (checkpoints fall at absolute multiples of the interval).
         Returns (o [T,H,dv], new pool, checkpoints [cap,H,dk,dv] or None)."""
         q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
         cu, sl = _i64(cu_seqlens), _i64(slots)
@@ -118,21 +128,23 @@ class Oracle:
         assert cu[0] == 0 and cu[-1] <= T
         hi = None if has_init is None else np.ascontiguousarray(
             np.asarray(has_init.cpu() if hasattr(has_init, "cpu") else has_init), dtype=np.uint8)
+        sp = None if start_pos is None else _i64(start_pos)
         ck = None
         if ckpt_interval > 0:
             lens = np.diff(cu)
+            p0 = np.zeros(n, np.int64) if sp is None else sp
             if ckpt_capacity is None:
-                ckpt_capacity = int((lens // ckpt_interval).sum())
+                ckpt_capacity = int(((p0 + lens) // ckpt_interval - p0 // ckpt_interval).sum())
             ck = np.full((ckpt_capacity, H, dk, dv), np.nan)
         o = np.full((T, H, dv), np.nan)   # rows of no sequence stay NaN
-        rc = self.lib.kda_oracle_prefill(
+        rc = self.lib.kda_oracle_prefill_at(
             _ptr(q, _f64p), _ptr(k, _f64p), _ptr(v, _f64p), _ptr(g, _f64p), _ptr(beta, _f64p),
             _ptr(cu, _i64p), n, H, dk, dv,
-            _ptr(pool, _f64p), pool.shape[0], _ptr(sl, _i64p), _ptr(hi, _u8p),
+            _ptr(pool, _f64p), pool.shape[0], _ptr(sl, _i64p), _ptr(hi, _u8p), _ptr(sp, _i64p),
             _ptr(ck, _f64p), 0 if ck is None else ck.shape[0], int(ckpt_interval),
             float(scale), int(bool(l2norm_qk)), float(l2_eps), _ptr(o, _f64p))
         if rc != 0:
-            raise ValueError(f"kda_oracle_prefill failed with status {rc}")
+            raise ValueError(f"kda_oracle_prefill_at failed with status {rc}")
         return o, pool, ck
 
     def decode(self, q, k, v, g, beta, pool, slots, scale: float = 1.0,

@@ -118,29 +118,39 @@ static void kda_token(double* S, int64_t dk, int64_t dv,
  *   slots : [n_seqs]; < 0 marks a graph-padding sequence
  *   has_init : [n_seqs] or NULL (all sequences have a state)
  *   ckpt : [ckpt_capacity, H, dk, dv] or NULL; ckpt_interval 0 = none
+ *   start_pos : [n_seqs] or NULL (all 0): absolute position of each
+ *          sequence's first token of this call (tokens processed before it,
+ *          e.g. a cached prefix).  A checkpoint is the state after every
+ *          token whose absolute count of processed tokens, start_pos + r + 1,
+ *          is a multiple of ckpt_interval; rows are laid out sequence by
+ *          sequence.
  *   l2norm_qk : normalise q and k per (token, head) before use
  */
-int kda_oracle_prefill(const double* q, const double* k, const double* v,
-                       const double* g, const double* beta,
-                       const int64_t* cu_seqlens, int64_t n_seqs,
-                       int64_t H, int64_t dk, int64_t dv,
-                       double* pool, int64_t n_slots, const int64_t* slots,
-                       const uint8_t* has_init,
-                       double* ckpt, int64_t ckpt_capacity, int64_t ckpt_interval,
-                       double scale, int l2norm_qk, double l2_eps, double* o)
+int kda_oracle_prefill_at(const double* q, const double* k, const double* v,
+                          const double* g, const double* beta,
+                          const int64_t* cu_seqlens, int64_t n_seqs,
+                          int64_t H, int64_t dk, int64_t dv,
+                          double* pool, int64_t n_slots, const int64_t* slots,
+                          const uint8_t* has_init, const int64_t* start_pos,
+                          double* ckpt, int64_t ckpt_capacity, int64_t ckpt_interval,
+                          double scale, int l2norm_qk, double l2_eps, double* o)
 {
     if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || ckpt_interval < 0)
         return ORACLE_EINVAL;
     for (int64_t i = 0; i < n_seqs; ++i) {
         if (cu_seqlens[i + 1] < cu_seqlens[i]) return ORACLE_EINVAL;
         if (slots[i] >= n_slots) return ORACLE_EINVAL;
+        if (start_pos && start_pos[i] < 0) return ORACLE_EINVAL;
     }
-    /* Checkpoint row where each sequence starts. */
+    /* Checkpoint row where each sequence starts: the multiples of the
+     * interval in (start, start + L]. */
     int64_t* ckpt_base = (int64_t*)calloc((size_t)n_seqs + 1, sizeof(int64_t));
     if (!ckpt_base) return ORACLE_ENOMEM;
     for (int64_t i = 0; i < n_seqs; ++i) {
         int64_t L = cu_seqlens[i + 1] - cu_seqlens[i];
-        ckpt_base[i + 1] = ckpt_base[i] + (ckpt_interval > 0 ? L / ckpt_interval : 0);
+        int64_t p0 = start_pos ? start_pos[i] : 0;
+        ckpt_base[i + 1] = ckpt_base[i] +
+                           (ckpt_interval > 0 ? (p0 + L) / ckpt_interval - p0 / ckpt_interval : 0);
     }
     const int64_t state_sz = dk * dv;
     int status = ORACLE_OK;
@@ -149,6 +159,7 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v,
     for (int64_t unit = 0; unit < n_seqs * H; ++unit) {
         const int64_t i = unit / H, h = unit % H;
         const int64_t t0 = cu_seqlens[i], L = cu_seqlens[i + 1] - cu_seqlens[i];
+        const int64_t p0 = start_pos ? start_pos[i] : 0;
         const int64_t slot = slots[i];
         if (slot < 0) {                                   /* padding: zero rows */
             for (int64_t t = t0; t < t0 + L; ++t)
@@ -180,8 +191,9 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v,
             }
             kda_token(S, dk, dv, qt, kt, v + (t * H + h) * dv, g + (t * H + h) * dk,
                       beta[t * H + h], scale, o + (t * H + h) * dv, work);
-            if (ckpt && ckpt_interval > 0 && (r + 1) % ckpt_interval == 0) {
-                int64_t row = ckpt_base[i] + (r + 1) / ckpt_interval - 1;
+            const int64_t pos = p0 + r + 1;            /* tokens processed so far */
+            if (ckpt && ckpt_interval > 0 && pos % ckpt_interval == 0) {
+                int64_t row = ckpt_base[i] + pos / ckpt_interval - p0 / ckpt_interval - 1;
                 if (row >= 0 && row < ckpt_capacity)
                     memcpy(ckpt + (row * H + h) * state_sz, S, (size_t)state_sz * sizeof(double));
             }
@@ -191,6 +203,21 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v,
     }
     free(ckpt_base);
     return status;
+}
+
+/* kda_oracle_prefill_at with every sequence starting at position 0. */
+int kda_oracle_prefill(const double* q, const double* k, const double* v,
+                       const double* g, const double* beta,
+                       const int64_t* cu_seqlens, int64_t n_seqs,
+                       int64_t H, int64_t dk, int64_t dv,
+                       double* pool, int64_t n_slots, const int64_t* slots,
+                       const uint8_t* has_init,
+                       double* ckpt, int64_t ckpt_capacity, int64_t ckpt_interval,
+                       double scale, int l2norm_qk, double l2_eps, double* o)
+{
+    return kda_oracle_prefill_at(q, k, v, g, beta, cu_seqlens, n_seqs, H, dk, dv, pool, n_slots,
+                                 slots, has_init, NULL, ckpt, ckpt_capacity, ckpt_interval, scale,
+                                 l2norm_qk, l2_eps, o);
 }
 
 /*

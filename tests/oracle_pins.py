@@ -16,6 +16,8 @@ algorithm):
   chunk_form         the chunked algebra (second algorithm) at C = 1..64
   split_calls        one call equals the same tokens split over calls via the pool
   checkpoints        checkpoint j equals the final state of a call cut at j*interval
+  checkpoints_absolute with start positions: rows at absolute multiples of the
+                     interval, each the state after that prefix; split calls agree
   decode             decode equals one-token prefill
   padding_empty      slot < 0 and empty sequences touch nothing
   has_init           has_initial_state = 0 equals a zeroed slot
@@ -216,6 +218,40 @@ def pin_checkpoints(orc):
             row += 1
 
 
+def pin_checkpoints_absolute(orc):
+    """With start positions, checkpoint rows fall where start + tokens
+    processed is a multiple of the interval (rows sequence by sequence), and
+    each equals the state after that prefix of the call; a sequence split
+    over two calls at a point off the interval grid gives the same
+    checkpoints as one call."""
+    rng = np.random.default_rng(116)
+    lens, start, iv = [11, 6, 9, 0], [3, 0, 13, 5], 4
+    T, H, dk, dv = sum(lens), 2, 4, 3
+    q, k, v, g, beta = _rand_case(rng, T, H, dk, dv)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pool = rng.standard_normal((4, H, dk, dv))
+    slots = [1, 3, 0, 2]
+    _, _, ck = orc.prefill(q, k, v, g, beta, cu, pool, slots, ckpt_interval=iv, start_pos=start)
+    assert ck.shape[0] == 3 + 1 + 2 + 0, f"checkpoint rows {ck.shape[0]}"
+    row = 0
+    for i, L in enumerate(lens):
+        for p in range(start[i] + 1, start[i] + L + 1):
+            if p % iv:
+                continue
+            t0, t1 = cu[i], cu[i] + p - start[i]
+            _, pj, _ = orc.prefill(q[t0:t1], k[t0:t1], v[t0:t1], g[t0:t1], beta[t0:t1],
+                                   [0, t1 - t0], pool, [slots[i]])
+            _close(ck[row], pj[slots[i]], 1e-13, f"checkpoint at position {p} of sequence {i}")
+            row += 1
+    # Sequence 0 (start 3) as two calls of 5 and 6 tokens.
+    _, p1, c1 = orc.prefill(q[:5], k[:5], v[:5], g[:5], beta[:5], [0, 5], pool, [1],
+                            ckpt_interval=iv, start_pos=[3])
+    _, _, c2 = orc.prefill(q[5:11], k[5:11], v[5:11], g[5:11], beta[5:11], [0, 6], p1, [1],
+                           ckpt_interval=iv, start_pos=[8])
+    assert c1.shape[0] == 2 and c2.shape[0] == 1
+    _close(np.concatenate([c1, c2]), ck[:3], 1e-13, "split calls: same absolute checkpoints")
+
+
 def pin_decode(orc):
     rng = np.random.default_rng(108)
     B, H, dk, dv = 7, 3, 5, 4
@@ -399,6 +435,7 @@ def pin_spec_decode(orc):
 
 
 ALL_PINS = [pin_hand_worked, pin_beta_zero, pin_exact_retrieval, pin_delta_invariant,
-            pin_linearity, pin_chunk_form, pin_split_calls, pin_checkpoints, pin_decode,
+            pin_linearity, pin_chunk_form, pin_split_calls, pin_checkpoints,
+            pin_checkpoints_absolute, pin_decode,
             pin_padding_empty, pin_has_init, pin_l2norm, pin_conv_numpy, pin_conv_state,
             pin_rmsnorm_library, pin_rmsnorm_variants, pin_spec_decode]

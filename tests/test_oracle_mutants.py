@@ -48,7 +48,10 @@ MUTANTS = {
                                "S[i * dv + j] += k[i] * v[j];"),
     "projection_uses_q": _sub("s += k[i] * S[i * dv + j];", "s += q[i] * S[i * dv + j];"),
     "scale_dropped": _sub("o[j] = scale * s;", "o[j] = s;"),
-    "checkpoint_off_by_one": _sub("(r + 1) % ckpt_interval == 0", "r % ckpt_interval == 0"),
+    "checkpoint_off_by_one": _sub("const int64_t pos = p0 + r + 1;", "const int64_t pos = p0 + r;"),
+    "checkpoint_ignores_start": _sub("const int64_t pos = p0 + r + 1;", "const int64_t pos = r + 1;"),
+    "checkpoint_rows_ignore_start": _sub("pos / ckpt_interval - p0 / ckpt_interval - 1",
+                                         "pos / ckpt_interval - 1"),
     "initial_state_ignored": _sub("if (!has_init || has_init[i]) memcpy(S, home",
                                   "if (1) memcpy(S, home"),
     "state_not_written": _sub("memcpy(home, S,", "if (0) memcpy(home, S,"),
