@@ -10,6 +10,7 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 bool dtype_ok(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
 bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64; }
@@ -118,6 +119,7 @@ kda_status_t prefill_common(
     a.out = out; a.out_stride = out_stride_t;
     a.workspace = workspace;
     a.act = act_dtype; a.state = state_dtype;
+    a.seq_pos = nullptr;
     a.conv_w = a.conv_b = nullptr; a.conv_state = nullptr;
     a.conv_width = 0; a.conv_flags = 0;
     a.ev[0] = a.ev[1] = a.ev[2] = nullptr;
@@ -150,6 +152,31 @@ kda_status_t kda_chunk_prefill(
         has_initial_state, checkpoints, ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out,
         out_stride_t, workspace, workspace_bytes);
     if (st != KDA_OK || num_seqs == 0) return st;
+    return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_chunk_prefill_at(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, const int64_t* seq_start_pos, int32_t num_seqs,
+    int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda::PrefillArgs a;
+    const kda_status_t st = prefill_common(
+        a, q, k, v, act_dtype, q_stride_t, k_stride_t, v_stride_t, g, beta, cu_seqlens, num_seqs,
+        total_tokens, num_heads, dk, dv, state_pool, state_dtype, num_slots, state_indices,
+        has_initial_state, checkpoints, ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out,
+        out_stride_t, workspace, workspace_bytes);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    if (!aligned8(seq_start_pos)) return KDA_ERR_INVALID_ARG;
+    a.seq_pos = seq_start_pos;
     return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

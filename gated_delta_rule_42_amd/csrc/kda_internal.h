@@ -50,6 +50,10 @@ struct PrefillArgs {
     void* out; int64_t out_stride;
     void* workspace;
     kda_dtype_t act, state;
+    // Absolute position of each sequence's first token ([num_seqs], device)
+    // or null (all 0): chunk boundaries and checkpoints follow absolute
+    // positions.
+    const int64_t* seq_pos;
     // Fused front end (conv_width > 0): q, k, v point into the packed
     // projection x and are taken through the causal conv1d first; its state
     // pool is indexed like the state pool (same slots, has_init, num_slots).

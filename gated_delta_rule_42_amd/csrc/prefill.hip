@@ -85,9 +85,12 @@ struct Shape {
     static_assert(D % 16 == 0 && D <= 128, "head dim");
 };
 
+// Upper bound on the chunks of a call: with absolute start positions a
+// sequence of L tokens spans at most floor(L / chunk) + 2 chunks (a partial
+// one at each end).
 int64_t max_chunks(int32_t num_seqs, int64_t total_tokens, int32_t chunk)
 {
-    return (total_tokens + chunk - 1) / chunk + num_seqs;
+    return (total_tokens + chunk - 1) / chunk + 2 * (int64_t)num_seqs;
 }
 
 // Eight consecutive activations (16 B bf16 / 32 B fp32) widened to fp32.
@@ -105,18 +108,32 @@ __device__ __forceinline__ void load8(const bf16* p, float (&x)[8])
     for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(t[i]);
 }
 
-__device__ __forceinline__ int num_chunks(int len, int bt) { return len > 0 ? (len + bt - 1) / bt : 0; }
+// Chunk geometry.  Chunk boundaries fall on absolute multiples of bt: a
+// sequence whose first token sits at absolute position p0 (tokens processed
+// before this call; 0 without positions) has a first chunk of bt - p0 % bt
+// tokens, then full chunks, then a partial one.  off = p0 % bt; negative
+// positions count as 0.
+__device__ __forceinline__ int64_t start_pos(const int64_t* __restrict__ pos, int i)
+{
+    return pos ? max<int64_t>(pos[i], 0) : 0;
+}
+__device__ __forceinline__ int num_chunks(int len, int bt, int off)
+{
+    return len > 0 ? (len + off + bt - 1) / bt : 0;
+}
+__device__ __forceinline__ int chunk_begin(int c, int bt, int off) { return c == 0 ? 0 : c * bt - off; }
+__device__ __forceinline__ int chunk_end(int c, int len, int bt, int off) { return min(len, (c + 1) * bt - off); }
 
 // The sequence that owns global chunk x (chunks numbered sequence by sequence)
 // and the index of that sequence's first chunk.  Whole-wave call; false if x
 // is past the last chunk.
-__device__ bool locate_chunk(const int32_t* __restrict__ cu, int n, int bt, int x, int lane,
-                             int& seq, int& first)
+__device__ bool locate_chunk(const int32_t* __restrict__ cu, const int64_t* __restrict__ pos, int n,
+                             int bt, int x, int lane, int& seq, int& first)
 {
     int base = 0;
     for (int i0 = 0; i0 < n; i0 += kWave) {
         const int i = i0 + lane;
-        const int nch = i < n ? num_chunks(cu[i + 1] - cu[i], bt) : 0;
+        const int nch = i < n ? num_chunks(cu[i + 1] - cu[i], bt, (int)(start_pos(pos, i) % bt)) : 0;
         const int incl = wave_inclusive_scan(nch, lane);
         const int excl = base + incl - nch;
         const unsigned long long hit = __ballot(i < n && x >= excl && x < excl + nch);
@@ -132,9 +149,10 @@ __device__ bool locate_chunk(const int32_t* __restrict__ cu, int n, int bt, int 
 }
 
 // Sums over the sequences before `seq`: their chunk count and their
-// checkpoint count.  Whole-wave call.
-__device__ void sequence_bases(const int32_t* __restrict__ cu, int seq, int bt, int interval,
-                               int lane, int& chunk_base, int64_t& ckpt_base)
+// checkpoint count (the multiples of the interval in (p0, p0 + len]).
+// Whole-wave call.
+__device__ void sequence_bases(const int32_t* __restrict__ cu, const int64_t* __restrict__ pos, int seq,
+                               int bt, int interval, int lane, int& chunk_base, int64_t& ckpt_base)
 {
     int cb = 0;
     int64_t kb = 0;
@@ -144,8 +162,9 @@ __device__ void sequence_bases(const int32_t* __restrict__ cu, int seq, int bt, 
         int64_t nck = 0;
         if (i < seq) {
             const int len = cu[i + 1] - cu[i];
-            nch = num_chunks(len, bt);
-            nck = (interval > 0 && len > 0) ? len / interval : 0;
+            const int64_t p0 = start_pos(pos, i);
+            nch = num_chunks(len, bt, (int)(p0 % bt));
+            nck = (interval > 0 && len > 0) ? (p0 + len) / interval - p0 / interval : 0;
         }
         cb += nch;
         kb += nck;
@@ -429,7 +448,8 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                   int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ g,
                   const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
                   int heads, const int32_t* __restrict__ slots, uint32_t flags,
-                  uint8_t* __restrict__ ws, int64_t flag_off, int64_t n_flags, ConvIn<AT> cv)
+                  const int64_t* __restrict__ pos, uint8_t* __restrict__ ws, int64_t flag_off,
+                  int64_t n_flags, ConvIn<AT> cv)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NKK = P::NKK_K;
@@ -474,10 +494,12 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
         for (int64_t i = ((int64_t)h * gridDim.x + x) * kWave + lane; i < n_flags; i += nwg * kWave) fl[i] = 0;
     }
     int seq = 0, first = 0;
-    if (!locate_chunk(cu, n_seqs, BT, x, lane, seq, first)) return;
+    if (!locate_chunk(cu, pos, n_seqs, BT, x, lane, seq, first)) return;
     if (slots[seq] < 0) return;              // padding sequence: nothing to precompute
-    const int64_t t0 = (int64_t)cu[seq] + (int64_t)(x - first) * BT;
-    const int len = (int)min<int64_t>(BT, (int64_t)cu[seq + 1] - t0);
+    const int off = (int)(start_pos(pos, seq) % BT);
+    const int cb = chunk_begin(x - first, BT, off);
+    const int64_t t0 = (int64_t)cu[seq] + cb;
+    const int len = chunk_end(x - first, cu[seq + 1] - cu[seq], BT, off) - cb;
 
     uint8_t* rec = ws + ((int64_t)x * heads + h) * P::REC_BYTES;
     bf16* wQ = reinterpret_cast<bf16*>(rec) + P::OFF_Q;
@@ -1036,7 +1058,7 @@ __device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, 
 
 template <int D, int BT, typename AT, typename ST>
 __global__ __launch_bounds__(kChainThreads)
-void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
+void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ pos, int n_seqs, int heads,
                   ST* __restrict__ pool, int64_t num_slots, const int32_t* __restrict__ slots,
                   const uint8_t* __restrict__ has_init, ST* __restrict__ ckpt, int64_t ckpt_cap,
                   int interval, float scale, AT* __restrict__ out, int64_t os,
@@ -1081,8 +1103,10 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
 
     int chunk_base = 0;
     int64_t ckpt_base = 0;
-    sequence_bases(cu, seq, BT, interval, lane, chunk_base, ckpt_base);
-    const int nch = num_chunks(len, BT);
+    sequence_bases(cu, pos, seq, BT, interval, lane, chunk_base, ckpt_base);
+    const int64_t p0 = start_pos(pos, seq);
+    const int off = (int)(p0 % BT);
+    const int nch = num_chunks(len, BT, off);
     // Chunks past the last are clamped to it, so prefetches stay in bounds.
     auto record = [&](int lc) {
         return reinterpret_cast<const bf16*>(
@@ -1190,9 +1214,10 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 }
                 *reinterpret_cast<bf16x4*>(&sS[l16][16 * kt + 4 * g4]) = s4;
             }
-            const int pos = (lc + 1) * BT;         // checkpoint at this chunk's end
-            if (ckpt && interval > 0 && pos <= len && pos % interval == 0) {
-                const int64_t row = ckpt_base + pos / interval - 1;
+            // Checkpoint where this chunk ends on an absolute multiple of the interval.
+            const int64_t at = p0 + chunk_end(lc, len, BT, off);
+            if (ckpt && interval > 0 && at % interval == 0) {
+                const int64_t row = ckpt_base + at / interval - p0 / interval - 1;
                 if (row < ckpt_cap) {
                     ST* dst = ckpt + (row * heads + h) * (int64_t)(D * D);
 #pragma unroll
@@ -1313,8 +1338,9 @@ void chain_kernel(const int32_t* __restrict__ cu, int n_seqs, int heads,
                 if (kk <= kmax)
                     acc0 = mfma16x16x32(*reinterpret_cast<const bf16x8*>(x + XS_BYTES + (kk * kWave + lane) * 16),
                                         o.a[kk], acc0);
-            const int64_t tc = s_begin + (int64_t)lc * BT;
-            if (r < min(BT, len - lc * BT)) {
+            const int cbeg = chunk_begin(lc, BT, off);
+            const int64_t tc = s_begin + cbeg;
+            if (r < chunk_end(lc, len, BT, off) - cbeg) {
                 const float bad = sBroken ? __builtin_nanf("") : 1.0f;
                 float o4[4];
 #pragma unroll
@@ -1379,13 +1405,15 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags, cv);
+                               a.seq_pos, static_cast<uint8_t*>(a.workspace), lay.flag_off,
+                               lay.n_flags, cv);
         else
             hipLaunchKernelGGL((intra_kernel<D, BT, AT, false>), grid, dim3(kThreads), 0, stream,
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               static_cast<uint8_t*>(a.workspace), lay.flag_off, lay.n_flags, cv);
+                               a.seq_pos, static_cast<uint8_t*>(a.workspace), lay.flag_off,
+                               lay.n_flags, cv);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1394,7 +1422,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST>), dim3((unsigned)pairs, (unsigned)(D / 16), 2u),
-                       dim3(kChainThreads), 0, stream, a.cu_seqlens, a.num_seqs, a.heads,
+                       dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                        static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                        static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
                        static_cast<AT*>(a.out), a.out_stride, static_cast<uint8_t*>(a.workspace),

@@ -58,6 +58,13 @@ def _load() -> ctypes.CDLL:
         vp, i32, i64, vp, vp,
         vp, i64, i32,
         f32, i32, u32, vp, i64, vp, sz, vp]
+    lib.kda_chunk_prefill_at.restype = i32
+    lib.kda_chunk_prefill_at.argtypes = [
+        vp, vp, vp, i32, i64, i64, i64, vp, vp,
+        vp, vp, i32, i64, i32, i32, i32,
+        vp, i32, i64, vp, vp,
+        vp, i64, i32,
+        f32, i32, u32, vp, i64, vp, sz, vp]
     lib.kda_conv_chunk_prefill.restype = i32
     lib.kda_conv_chunk_prefill.argtypes = [
         vp, i64, i32, vp, vp, i32, u32, vp, vp, vp,
@@ -154,6 +161,27 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, 
     int32; has_initial_state [N] uint8 or None; checkpoints [cap,H,dk,dv] or
     None.  `workspace` is a uint8 tensor of at least
     chunk_prefill_workspace_size(...) bytes; None allocates one."""
+    _prefill_call(None, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
+                  workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
+                  flags, stream)
+
+
+def chunk_prefill_at(q, k, v, g, beta, cu_seqlens, seq_start_pos, state_pool, state_indices,
+                     out, *, workspace=None, has_initial_state=None, checkpoints=None,
+                     ckpt_interval: int = 0, scale: float = 1.0, chunk_size: int = 64,
+                     flags: int = 0, stream=None) -> None:
+    """kda_chunk_prefill_at: chunk_prefill for sequences starting at absolute
+    positions seq_start_pos [N] int64 (device; chunk boundaries and
+    checkpoints follow absolute positions)."""
+    _contig(seq_start_pos, "seq_start_pos", torch.int64)
+    _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
+                  workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
+                  flags, stream)
+
+
+def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
+                  workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
+                  flags, stream) -> None:
     T, H, dk = q.shape
     dv = v.shape[2]
     N = state_indices.numel()
@@ -173,17 +201,21 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, 
         if not checkpoints.is_contiguous() or checkpoints.dtype != state_pool.dtype:
             raise ValueError("checkpoints must be contiguous with the state dtype")
         cap = checkpoints.shape[0]
-    status = _lib.kda_chunk_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _dtype(q),
-        _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v"),
-        _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
-        _ptr(state_pool), _dtype(state_pool), state_pool.shape[0] if state_pool.dim() else 0,
-        _ptr(state_indices), _ptr(has_initial_state),
-        _ptr(checkpoints), cap, int(ckpt_interval),
-        float(scale), int(chunk_size), int(flags),
-        _ptr(out), _token_stride(out, "out"),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("kda_chunk_prefill", status)
+    head = (_ptr(q), _ptr(k), _ptr(v), _dtype(q),
+            _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v"),
+            _ptr(g), _ptr(beta), _ptr(cu_seqlens))
+    tail = (T, H, dk, dv,
+            _ptr(state_pool), _dtype(state_pool), state_pool.shape[0] if state_pool.dim() else 0,
+            _ptr(state_indices), _ptr(has_initial_state),
+            _ptr(checkpoints), cap, int(ckpt_interval),
+            float(scale), int(chunk_size), int(flags),
+            _ptr(out), _token_stride(out, "out"),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if seq_start_pos is None:
+        _check("kda_chunk_prefill", _lib.kda_chunk_prefill(*head, N, *tail))
+    else:
+        _check("kda_chunk_prefill_at",
+               _lib.kda_chunk_prefill_at(*head, _ptr(seq_start_pos), N, *tail))
 
 
 def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, state_pool,

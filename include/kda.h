@@ -252,6 +252,35 @@ kda_status_t kda_causal_conv1d(
     void* y, int64_t y_stride_t, void* stream);
 
 /*
+ * Chunk prefill of sequences that start at absolute positions (page
+ * "FlashKDA kernel upgrade supports bf16 checkpoint state", function and
+ * motivation: checkpoint states are the breakpoints that join the recurrent
+ * state across segments, so they belong to absolute positions of a
+ * sequence, e.g. aligned with a cached prefix).
+ *   seq_start_pos [num_seqs] int64, device, or NULL (all 0): tokens of each
+ *            sequence processed before this call; negative values count as 0.
+ * Chunk boundaries fall on absolute multiples of chunk_size (a sequence's
+ * first chunk holds chunk_size - start % chunk_size tokens), and checkpoint
+ * rows hold the state after every token whose absolute count
+ * start + (tokens of this call so far) is a multiple of ckpt_interval: the
+ * multiples of the interval in (start, start + L] for a sequence of L tokens,
+ * rows laid out sequence by sequence.  Everything else is kda_chunk_prefill
+ * (same workspace query); with all positions 0 the results are identical.
+ */
+kda_status_t kda_chunk_prefill_at(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, const int64_t* seq_start_pos, int32_t num_seqs,
+    int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fused front end + chunk prefill: kda_causal_conv1d over the packed
  * projection x = [q | k | v] followed by kda_chunk_prefill on its three parts,
  * with the convolution evaluated where the prefill loads its activations, so

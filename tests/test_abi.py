@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_chunk_prefill", "kda_recurrent_decode", "kda_gated_rmsnorm",
                  "kda_causal_conv1d", "kda_chunk_prefill_workspace_size",
-                 "kda_conv_chunk_prefill", "kda_gated_rmsnorm_ex", "kda_spec_decode", "kda_spec_commit",
+                 "kda_conv_chunk_prefill", "kda_gated_rmsnorm_ex", "kda_chunk_prefill_at",
+                 "kda_spec_decode", "kda_spec_commit",
                  "kda_abi_version", "kda_status_string"):
         assert want in names
 
@@ -62,12 +63,14 @@ def test_workspace_size(lib):
     one = kda.chunk_prefill_workspace_size(1, 64, 1, 128, 128, 64)
     assert one > 0 and one % 256 == 0
     # Per (chunk slot, head): one record and the chain's exchange slots (one per
-    # 16-column tile); chunk slots = ceil(T / C) + N.  Then one 32-bit flag per
-    # (sequence, head, tile), rounded up to 256 bytes.
+    # 16-column tile); chunk slots = ceil(T / C) + 2 N (a sequence starting at
+    # an absolute position off the chunk grid has a partial chunk at each
+    # end).  Then one 32-bit flag per (sequence, head, tile), rounded up to
+    # 256 bytes.
     flags = lambda n, h: (n * h * (128 // 16) * 4 + 255) // 256 * 256
-    per_slot = (one - flags(1, 1)) // 2
+    per_slot = (one - flags(1, 1)) // 3
     assert per_slot == 74240 + 8 * 16 * (128 + 64) * 2
-    assert kda.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64) == (64 + 1) * 16 * per_slot + flags(1, 16)
+    assert kda.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64) == (64 + 2) * 16 * per_slot + flags(1, 16)
     assert kda.chunk_prefill_workspace_size(3, 100, 2, 64, 64, 32) > 0
     for bad in [(1, 64, 1, 48, 48, 64), (1, 64, 1, 128, 64, 64), (1, 64, 1, 128, 128, 48),
                 (-1, 64, 1, 128, 128, 64), (1, 64, 0, 128, 128, 64)]:
@@ -118,6 +121,19 @@ def _conv_prefill(lib, **over):
              out=FAKE, os=2048, ws=FAKE, wsb=0, stream=None)
     a.update(over)
     return lib.kda_conv_chunk_prefill(*a.values())
+
+
+def test_prefill_at_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+    need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, act=1, qs=2048, ks=2048, vs=2048, g=FAKE, beta=FAKE,
+             cu=FAKE, pos=FAKE + 4, n=1, T=64, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=4,
+             idx=FAKE, hi=None, ck=None, cap=0, interval=0, scale=1.0, C=64, flags=0, out=FAKE,
+             os=2048, ws=FAKE, wsb=need, stream=None)
+    assert lib.kda_chunk_prefill_at(*a.values()) == K.KDA_ERR_INVALID_ARG    # misaligned positions
+    assert lib.kda_chunk_prefill_at(*dict(a, n=0).values()) == K.KDA_OK
+    assert lib.kda_chunk_prefill_at(*dict(a, interval=100).values()) == K.KDA_ERR_UNSUPPORTED
+    assert lib.kda_chunk_prefill_at(*dict(a, wsb=100).values()) == K.KDA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_conv_prefill_validation(lib):
