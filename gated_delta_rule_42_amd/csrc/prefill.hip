@@ -1122,6 +1122,17 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
         ST* home = pool + ((int64_t)slot * heads + h) * (int64_t)(D * D);
         const bool dwave = wave < NS;              // owns a token tile of D
         const int tt = dwave ? wave : 0;
+        // The initial state, every address clamped into the state so that the
+        // loads carry no per-element branch and issue together (a branch per
+        // element makes each load wait for the one before).
+        ST s0[NKT_W][4];
+#pragma unroll
+        for (int j = 0; j < NKT_W; ++j)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int row = min(16 * (wave + 4 * j) + 4 * g4 + ii, D - 1);
+                s0[j][ii] = init ? home[(int64_t)row * D + col] : from_f32<ST>(0.0f);
+            }
         float S[NKT_W][4];
 #pragma unroll
         for (int j = 0; j < NKT_W; ++j) {
@@ -1129,7 +1140,7 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int row = 16 * kt + 4 * g4 + ii;
-                S[j][ii] = (init && kt < P::NMT_K && row < D) ? to_f32(home[(int64_t)row * D + col]) : 0.0f;
+                S[j][ii] = (kt < P::NMT_K && row < D) ? to_f32(s0[j][ii]) : 0.0f;
             }
             if (kt < P::NMT_K) {
                 bf16x4 s4;
@@ -1164,8 +1175,29 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                     reinterpret_cast<const uint8_t*>(rec) + P::EG_BYTE_OFF + (16 * kt + 4 * g4) * 4);
             }
         };
+        // Checkpoint of chunk c (S holds the state after it) where the chunk
+        // ends on an absolute multiple of the interval.  Written at the start
+        // of the next step, before its refill, so that no store follows the
+        // refill's loads (the wait at the end of a step counts on that).
+        auto checkpoint = [&](int c) {
+            const int64_t at = p0 + chunk_end(c, len, BT, off);
+            if (!ckpt || interval <= 0 || at % interval != 0) return;
+            const int64_t row = ckpt_base + at / interval - p0 / interval - 1;
+            if (row >= ckpt_cap) return;
+            ST* dst = ckpt + (row * heads + h) * (int64_t)(D * D);
+#pragma unroll
+            for (int j = 0; j < NKT_W; ++j) {
+                const int kt = wave + 4 * j;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 16 * kt + 4 * g4 + ii;
+                    if (kt < P::NMT_K && rr < D) dst[(int64_t)rr * D + col] = from_f32<ST>(S[j][ii]);
+                }
+            }
+        };
         auto step = [&](int lc, const Ops& o, auto refill) {
             uint8_t* const slot_x = xch + (int64_t)lc * XSLOT;
+            if (lc > 0) checkpoint(lc - 1);
             // This chunk's S (its start state) to the exchange slot.
 #pragma unroll
             for (int j = 0; j < NKT_W; ++j) {
@@ -1214,26 +1246,9 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                 }
                 *reinterpret_cast<bf16x4*>(&sS[l16][16 * kt + 4 * g4]) = s4;
             }
-            // Checkpoint where this chunk ends on an absolute multiple of the interval.
-            const int64_t at = p0 + chunk_end(lc, len, BT, off);
-            if (ckpt && interval > 0 && at % interval == 0) {
-                const int64_t row = ckpt_base + at / interval - p0 / interval - 1;
-                if (row < ckpt_cap) {
-                    ST* dst = ckpt + (row * heads + h) * (int64_t)(D * D);
-#pragma unroll
-                    for (int j = 0; j < NKT_W; ++j) {
-                        const int kt = wave + 4 * j;
-#pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) {
-                            const int rr = 16 * kt + 4 * g4 + ii;
-                            if (kt < P::NMT_K && rr < D) dst[(int64_t)rr * D + col] = from_f32<ST>(S[j][ii]);
-                        }
-                    }
-                }
-            }
             // This step's exchange stores are older than the refill's LOADS
-            // loads, so they have reached L2 once at most LOADS (plus any newer
-            // checkpoint stores) remain outstanding.
+            // loads, so they have reached L2 once at most LOADS remain
+            // outstanding (no store follows the refill).
             asm volatile("" ::: "memory");
             wait_vmcnt<LOADS>();
             lds_barrier();                         // B2
@@ -1246,6 +1261,7 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
         for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
         lds_barrier();                             // B0: S_0 published
         run_steps<NB>(nch, buf, fetch, step);
+        checkpoint(nch - 1);
 #pragma unroll
         for (int j = 0; j < NKT_W; ++j) {          // final state, in place
             const int kt = wave + 4 * j;
