@@ -151,6 +151,21 @@ __device__ __forceinline__ float silu_f32(float a)
     return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
+// Gated RMSNorm arithmetic: 1 / rms from a row's sum of squares, and one
+// output element (h * inv * w + b) * act(z) with act(z) = z * sigmoid(z), or
+// sigmoid(z) when `sigmoid` (hardware reciprocal).
+__device__ __forceinline__ float rms_inv(float ss, int dim, float eps)
+{
+    return 1.0f / sqrtf(ss / (float)dim + eps);
+}
+__device__ __forceinline__ float gated_norm_out(float h, float inv, float w, float b, float z,
+                                                bool sigmoid)
+{
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+    const float act = sigmoid ? sg : z * sg;
+    return (h * inv * w + b) * act;
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8])
 {
     bf16x8 r;

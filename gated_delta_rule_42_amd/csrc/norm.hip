@@ -112,13 +112,13 @@ void gated_rmsnorm_kernel(const T* __restrict__ x, int64_t xs, const T* __restri
             row_vec(c, hv);
             if (ror) store8(ror + c, hv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss += hv[i] * hv[i];
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(hv[i], hv[i], ss);
         }
     }
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, LPR);
     if (!live) return;
-    const float inv = 1.0f / sqrtf(ss / (float)dim + eps);
+    const float inv = rms_inv(ss, dim, eps);
 
     for (int c = lane_in_row * 8; c < dim; c += LPR * 8) {
         float hv[8], gv[8], wv[8], bv[8], out[8];
@@ -137,13 +137,7 @@ void gated_rmsnorm_kernel(const T* __restrict__ x, int64_t xs, const T* __restri
             for (int i = 0; i < 8; ++i) bv[i] = 0.0f;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // sigmoid(z) with the hardware reciprocal (within 1 ulp).
-            const float z = gv[i];
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-            const float act = sig ? sg : z * sg;
-            out[i] = (hv[i] * inv * wv[i] + bv[i]) * act;
-        }
+        for (int i = 0; i < 8; ++i) out[i] = gated_norm_out(hv[i], inv, wv[i], bv[i], gv[i], sig);
         store8(yr + c, out);
     }
 }
