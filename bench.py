@@ -41,10 +41,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "6cd9219ae777c0e79e1cc36a363c97ff516347b361cec47f000e2f7d6b352f0f",
-              86792775, 73925120),
-    "chain": (_PREFILL_SRC, "6cd9219ae777c0e79e1cc36a363c97ff516347b361cec47f000e2f7d6b352f0f",
-              125656238, 68193690),
+    "intra": (_PREFILL_SRC, "94507ca68768bd079e147d75db1bf5ee426ac547d676c4292aa224d2be033394",
+              86805882, 73925120),
+    "chain": (_PREFILL_SRC, "94507ca68768bd079e147d75db1bf5ee426ac547d676c4292aa224d2be033394",
+              125719315, 68177510),
     "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
                547998632, 539217818),
 }
