@@ -230,6 +230,13 @@ __device__ __forceinline__ float dpp_row_shr(float x)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
         0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
 }
+// Lane QL of each group of four lanes, broadcast to the group.
+template <int QL>
+__device__ __forceinline__ float quad_bcast(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, x), QL * 0x55, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row_scan16(float x)
 {
     x += dpp_row_shr<1>(x);
@@ -1034,8 +1041,9 @@ __device__ __forceinline__ void consume(const T& x)
 // The chunk loop of one wave with a register ring of NB chunks.  The loop
 // runs whole groups of NB steps (so every buffer is used at a fixed place in
 // the body) and the last nch % NB steps after it.  Step lc runs on the buffer
-// of chunk lc and calls `refill` once, which starts the loads of chunk
-// lc + NB - 1 into the buffer that step lc - 1 used.
+// of chunk lc and calls `refill`, which starts the loads of chunk lc + NB - 1
+// into the buffer that step lc - 1 used (its arguments go on to `fetch`, so a
+// step may start them in parts).
 template <int NB, typename Ops, typename Fetch, typename Step>
 __device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, Step step)
 {
@@ -1044,14 +1052,14 @@ __device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, 
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
             consume(buf[u]);
-            step(c0 + u, buf[u], [&]() { fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB]); });
+            step(c0 + u, buf[u], [&](auto... part) { fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB], part...); });
         }
     }
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u) {
         if (c0 + u < nch) {
             consume(buf[u]);
-            step(c0 + u, buf[u], [&]() { fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB]); });
+            step(c0 + u, buf[u], [&](auto... part) { fetch(c0 + u + NB - 1, buf[(u + NB - 1) % NB], part...); });
         }
     }
 }
@@ -1156,29 +1164,51 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
             bf16x8 w[P::NKK_K];                    // W rows of token tile tt
             bf16x4 u;                              // U^T: column col, 4 tokens of tile tt
             bf16x8 kb[NKT_W][P::NKK_T];            // Kb^T rows of key tiles wave + 4 j
-            f32x4 eg[NKT_W];                       // e^{G_C} of those rows
+            float eg[NKT_W];                       // e^{G_C} of row 16 kt + 4 g4 + l16 % 4
         };
-        constexpr int LOADS = P::NKK_K + 1 + NKT_W * (P::NKK_T + 1);   // loads per fetch
-        auto fetch = [&](int lc, Ops& o) {
+        // A chunk's operands are fetched in three parts, spread over a step
+        // so that no one burst of loads fills the CU's memory queue and
+        // stalls the wave: W (part 0), U and e^{G_C} (part 1), Kb^T (part 2);
+        // part -1 is all three.  Every load is unconditional, so the counts
+        // below are exact.
+        constexpr int LOADS1 = 1 + NKT_W, LOADS2 = NKT_W * P::NKK_T;
+        constexpr int LOADS = P::NKK_K + LOADS1 + LOADS2;                 // loads per chunk
+        auto fetch = [&](int lc, Ops& o, auto part) {
+            constexpr int PART = decltype(part)::value;
             const bf16* rec = record(lc);
+            if constexpr (PART < 0 || PART == 0) {
 #pragma unroll
-            for (int kk = 0; kk < P::NKK_K; ++kk)
-                o.w[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_W + frag<DKP>(16 * tt + l16, 32 * kk + 8 * g4));
-            o.u = *reinterpret_cast<const bf16x4*>(rec + P::OFF_U + frag<BTP>(col, 16 * tt + 4 * g4));
+                for (int kk = 0; kk < P::NKK_K; ++kk)
+                    o.w[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_W + frag<DKP>(16 * tt + l16, 32 * kk + 8 * g4));
+            }
+            if constexpr (PART < 0 || PART == 1) {
+                o.u = *reinterpret_cast<const bf16x4*>(rec + P::OFF_U + frag<BTP>(col, 16 * tt + 4 * g4));
 #pragma unroll
-            for (int j = 0; j < NKT_W; ++j) {
-                const int kt = min(wave + 4 * j, P::NMT_K - 1);
+                for (int j = 0; j < NKT_W; ++j) {
+                    const int kt = min(wave + 4 * j, P::NMT_K - 1);
+                    // One float per lane, spread over the quad in the update:
+                    // a 16-byte load per lane would move 16 times the bytes.
+                    o.eg[j] = *reinterpret_cast<const float*>(
+                        reinterpret_cast<const uint8_t*>(rec) + P::EG_BYTE_OFF + (16 * kt + 4 * g4 + (l16 & 3)) * 4);
+                }
+            }
+            if constexpr (PART < 0 || PART == 2) {
 #pragma unroll
-                for (int kk = 0; kk < P::NKK_T; ++kk)
-                    o.kb[j][kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_KB + frag<BTP>(16 * kt + l16, 32 * kk + 8 * g4));
-                o.eg[j] = *reinterpret_cast<const f32x4*>(
-                    reinterpret_cast<const uint8_t*>(rec) + P::EG_BYTE_OFF + (16 * kt + 4 * g4) * 4);
+                for (int j = 0; j < NKT_W; ++j) {
+                    const int kt = min(wave + 4 * j, P::NMT_K - 1);
+#pragma unroll
+                    for (int kk = 0; kk < P::NKK_T; ++kk)
+                        o.kb[j][kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_KB + frag<BTP>(16 * kt + l16, 32 * kk + 8 * g4));
+                }
             }
         };
+        using Part0 = std::integral_constant<int, 0>;
+        using Part1 = std::integral_constant<int, 1>;
+        using Part2 = std::integral_constant<int, 2>;
+        using AllParts = std::integral_constant<int, -1>;
         // Checkpoint of chunk c (S holds the state after it) where the chunk
-        // ends on an absolute multiple of the interval.  Written at the start
-        // of the next step, before its refill, so that no store follows the
-        // refill's loads (the wait at the end of a step counts on that).
+        // ends on an absolute multiple of the interval, written at the start
+        // of the next step.
         auto checkpoint = [&](int c) {
             const int64_t at = p0 + chunk_end(c, len, BT, off);
             if (!ckpt || interval <= 0 || at % interval != 0) return;
@@ -1195,6 +1225,11 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                 }
             }
         };
+        // Publishes that chunks 0 .. n - 1 are in their exchange slots.
+        auto publish = [&](int n) {
+            if (wave == 0 && lane == 0)
+                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
         auto step = [&](int lc, const Ops& o, auto refill) {
             uint8_t* const slot_x = xch + (int64_t)lc * XSLOT;
             if (lc > 0) checkpoint(lc - 1);
@@ -1208,6 +1243,7 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                 for (int ii = 0; ii < 4; ++ii) s4[ii] = static_cast<bf16>(S[j][ii]);
                 *reinterpret_cast<bf16x4*>(slot_x + 2 * frag<DKP>(l16, 16 * kt + 4 * g4)) = s4;
             }
+            refill(Part0{});
             if (dwave) {                           // D = U - W S, token tile tt
                 f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1225,16 +1261,19 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
             }
             if (BTP > BT && wave == 0)             // token padding of D^T
                 *reinterpret_cast<bf16x4*>(slot_x + XS_BYTES + 2 * frag<BTP>(l16, BT + 4 * g4)) = bf16x4{};
-            asm volatile("" ::: "memory");         // the refill's loads come after the stores
-            refill();
+            asm volatile("" ::: "memory");         // parts 1 and 2 come after the stores
+            refill(Part1{});
             lds_barrier();                         // B1
+            refill(Part2{});
 #pragma unroll
             for (int j = 0; j < NKT_W; ++j) {      // S <- Diag(e^{G_C}) S + Kb^T D
                 const int kt = wave + 4 * j;
                 if (kt >= P::NMT_K) continue;
                 f32x4 acc;
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) acc[ii] = S[j][ii] * o.eg[j][ii];
+                acc[0] = S[j][0] * quad_bcast<0>(o.eg[j]);
+                acc[1] = S[j][1] * quad_bcast<1>(o.eg[j]);
+                acc[2] = S[j][2] * quad_bcast<2>(o.eg[j]);
+                acc[3] = S[j][3] * quad_bcast<3>(o.eg[j]);
 #pragma unroll
                 for (int kk = 0; kk < P::NKK_T; ++kk)
                     acc = mfma16x16x32(o.kb[j][kk], *reinterpret_cast<const bf16x8*>(&sD[l16][32 * kk + 8 * g4]), acc);
@@ -1246,21 +1285,24 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                 }
                 *reinterpret_cast<bf16x4*>(&sS[l16][16 * kt + 4 * g4]) = s4;
             }
-            // This step's exchange stores are older than the refill's LOADS
-            // loads, so they have reached L2 once at most LOADS remain
-            // outstanding (no store follows the refill).
+            // Chunk lc - 1 is published one step late, so that its stores are
+            // long done and the wait costs nothing: they are older than the
+            // previous step's parts 1 and 2 and all of this step's loads, so
+            // they have reached L2 once at most that many operations remain
+            // outstanding.
             asm volatile("" ::: "memory");
-            wait_vmcnt<LOADS>();
+            wait_vmcnt<LOADS1 + LOADS2 + LOADS>();
             lds_barrier();                         // B2
-            if (wave == 0 && lane == 0)
-                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)(lc + 1), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (lc > 0) publish(lc);
         };
         Ops buf[NB];
 #pragma unroll
-        for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
+        for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b], AllParts{});
         lds_barrier();                             // B0: S_0 published
         run_steps<NB>(nch, buf, fetch, step);
+        wait_vmcnt<0>();
+        lds_barrier();
+        publish(nch);
         checkpoint(nch - 1);
 #pragma unroll
         for (int j = 0; j < NKT_W; ++j) {          // final state, in place
