@@ -903,35 +903,49 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     }
     __syncthreads();                          // K~^T, V^T ready
 
-    // 5. Wave w: the rows of token tile w.  W^T = K~^T T^T (lane: 4
-    //    consecutive channels of one W row) and U = T V (lane: 4 consecutive
-    //    tokens of one U^T row); the T fragment is the same for every tile and
-    //    K stops at the diagonal block.
-    if (tok_wave) {
-        const int kmax = (16 * wave + 15) / 32;
-        bf16x8 tf[P::NKK_T];
+    // 5. W^T = K~^T T^T (lane: 4 consecutive channels of one W row) and
+    //    U = T V (lane: 4 consecutive tokens of one U^T row), K stopping at
+    //    each token tile's diagonal block.  Wave w takes the key tiles and the
+    //    value tiles w, w + 4, ... for every token tile: a later token tile
+    //    needs more K steps, so this spreads the products evenly, and each
+    //    K~^T or V^T fragment is read from LDS once per wave.
+    {
+        bf16x8 tf[NS][P::NKK_T];
 #pragma unroll
-        for (int kk = 0; kk < P::NKK_T; ++kk)
-            tf[kk] = kk <= kmax ? *reinterpret_cast<const bf16x8*>(&sT[r][32 * kk + 8 * g4]) : bf16x8{};
-#pragma unroll
-        for (int mt = 0; mt < DKP / 16; ++mt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NS; ++t)
 #pragma unroll
             for (int kk = 0; kk < P::NKK_T; ++kk)
-                if (kk <= kmax)
-                    acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sKt[16 * mt + l16][32 * kk + 8 * g4]),
-                                       tf[kk], acc);
-            *reinterpret_cast<bf16x4*>(wW + frag<DKP>(r, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
+                tf[t][kk] = kk <= (16 * t + 15) / 32
+                                ? *reinterpret_cast<const bf16x8*>(&sT[16 * t + l16][32 * kk + 8 * g4]) : bf16x8{};
+#pragma unroll
+        for (int mt = wave; mt < DKP / 16; mt += kThreads / kWave) {
+            bf16x8 kf[P::NKK_T];
+#pragma unroll
+            for (int kk = 0; kk < P::NKK_T; ++kk)
+                kf[kk] = *reinterpret_cast<const bf16x8*>(&sKt[16 * mt + l16][32 * kk + 8 * g4]);
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < P::NKK_T; ++kk)
+                    if (kk <= (16 * t + 15) / 32) acc = mfma16x16x32(kf[kk], tf[t][kk], acc);
+                *reinterpret_cast<bf16x4*>(wW + frag<DKP>(16 * t + l16, 16 * mt + 4 * g4)) = pack_bf16x4(acc);
+            }
         }
 #pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int nt = wave; nt < D / 16; nt += kThreads / kWave) {
+            bf16x8 vf[P::NKK_T];
 #pragma unroll
             for (int kk = 0; kk < P::NKK_T; ++kk)
-                if (kk <= kmax)
-                    acc = mfma16x16x32(tf[kk],
-                                       *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][32 * kk + 8 * g4]), acc);
-            *reinterpret_cast<bf16x4*>(wU + frag<BTP>(16 * nt + l16, 16 * wave + 4 * g4)) = pack_bf16x4(acc);
+                vf[kk] = *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + l16][32 * kk + 8 * g4]);
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < P::NKK_T; ++kk)
+                    if (kk <= (16 * t + 15) / 32) acc = mfma16x16x32(tf[t][kk], vf[kk], acc);
+                *reinterpret_cast<bf16x4*>(wU + frag<BTP>(16 * nt + l16, 16 * t + 4 * g4)) = pack_bf16x4(acc);
+            }
         }
     }
     if (BTP > BT)
