@@ -52,6 +52,9 @@ constexpr int kThreads = 256;   // four waves per workgroup
 // products use the chunk start as the only reference point: e^{80} and
 // e^{-80} are far inside the fp32 / bf16 range.
 constexpr float kMaxLogDecay = 80.0f;
+// Bound on a wave's wait for another wave of its workgroup (that wave writes
+// within a few hundred cycles; the bound only keeps every wait finite).
+constexpr int kMaxRowWait = 1 << 20;
 
 template <int D, int BT>
 struct Shape {
@@ -482,11 +485,15 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     auto sVt = reinterpret_cast<bf16 (*)[TP]>(sR2);                      // V^T [DKP][TP]
     __shared__ __attribute__((aligned(16))) float sXd[NS][16][20];       // diagonal blocks of X
     __shared__ __attribute__((aligned(16))) bf16 sT[BT][TP];             // T = X Diag(beta)
-    __shared__ __attribute__((aligned(16))) float sTot[4][DKP];          // tile totals of g
+    // Per-tile factors of the gate (dead once the Gram phase starts, when the
+    // same bytes hold the last token tile's row fragments).
+    __shared__ __attribute__((aligned(16))) float sFac[4][4][DKP];
+    auto& sTot = sFac[0];                                                // tile totals of g
     __shared__ __attribute__((aligned(16))) float sE[4][DKP];            // e^{tile total}
-    __shared__ __attribute__((aligned(16))) float sBef[4][DKP];          // e^{G_b}
-    __shared__ __attribute__((aligned(16))) float sAft[4][DKP];          // e^{G_C - G_b}
-    __shared__ __attribute__((aligned(16))) float sInv[4][DKP];          // e^{-G_b}
+    auto& sBef = sFac[1];                                                // e^{G_b}
+    auto& sAft = sFac[2];                                                // e^{G_C - G_b}
+    auto& sInv = sFac[3];                                                // e^{-G_b}
+    __shared__ int sRowsReady;                                           // sKr written
     __shared__ __attribute__((aligned(16))) float sBeta[BTP];
     __shared__ __attribute__((aligned(16))) float sCw[CONV ? 3 * kMaxConvWidth * D : 1];   // conv weights
 
@@ -659,6 +666,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     }
     if (tok_wave && g4 == 0) sBeta[r] = b_r;
     if (BTP > BT && tid < BTP - BT) sBeta[BT + tid] = 0.0f;
+    if (tid == 0) sRowsReady = 0;
 
     // 1. Cumulative gate inside the tile (DPP scan over the 16 token lanes).
 #pragma unroll
@@ -780,8 +788,35 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     //    Multi-reference (strong decay): the reference of block (w, j) is
     //    b_j; the row side is k_r f_j with f_j = f_{j+1} e^{tile total j} <= 1,
     //    the column side K^_s = k_s e^{G_{b_j} - G_s} written by wave j.
+    //    With four token tiles and a single reference, blocks (3, 0) and
+    //    (3, 1) go to waves 0 and 1, which read tile 3's row fragments from
+    //    LDS: no wave then does more than three blocks (instead of 1 .. 4).
+    auto gram_store = [&](int w, int j, const f32x4& ck, const f32x4& cq, float br) {
+        const int rr = 16 * w + l16;
+        f32x4 mk, aq;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int sc = 16 * j + 4 * g4 + ii;
+            mk[ii] = sc < rr ? br * ck[ii] : 0.0f;
+            aq[ii] = sc <= rr ? cq[ii] : 0.0f;
+        }
+        *reinterpret_cast<f32x4*>(&sM[rr][16 * j + 4 * g4]) = mk;
+        *reinterpret_cast<bf16x4*>(wA + aq_frag(rr, 16 * j + 4 * g4)) = pack_bf16x4(aq);
+    };
+    const bool split_gram = NS == 4 && !strong;
+    auto sKr = reinterpret_cast<bf16x8 (*)[NKK][kWave]>(&sFac[0][0][0]);   // [2][NKK][64]: K~, Q~ of tile 3
+    static_assert(sizeof(sFac) >= 2 * NKK * kWave * sizeof(bf16x8), "row fragments fit");
     if (tok_wave) {
-        for (int j = wave; j >= 0; --j) {
+        if (split_gram && wave == 3) {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                sKr[0][kk][lane] = kt0[kk];
+                sKr[1][kk][lane] = qt0[kk];
+            }
+            __hip_atomic_store(&sRowsReady, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        const int jmin = split_gram && wave == 3 ? 2 : 0;
+        for (int j = wave; j >= jmin; --j) {
             f32x4 ck = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
             if (!strong) {
 #pragma unroll
@@ -812,15 +847,21 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                     cq = mfma16x16x32(a, pack_bf16x8(bq), cq);
                 }
             }
-            f32x4 mk, aq;
+            gram_store(wave, j, ck, cq, b_r);
+        }
+        if (split_gram && wave < 2) {           // block (3, wave)
+            for (int spin = 0; spin < kMaxRowWait &&
+                               __hip_atomic_load(&sRowsReady, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+                 ++spin)
+                __builtin_amdgcn_s_sleep(1);
+            f32x4 ck = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int s = 16 * j + 4 * g4 + ii;
-                mk[ii] = s < r ? b_r * ck[ii] : 0.0f;
-                aq[ii] = s <= r ? cq[ii] : 0.0f;
+            for (int kk = 0; kk < NKK; ++kk) {
+                const bf16x8 a = sKh[wave][kk][lane];
+                ck = mfma16x16x32(a, sKr[0][kk][lane], ck);
+                cq = mfma16x16x32(a, sKr[1][kk][lane], cq);
             }
-            *reinterpret_cast<f32x4*>(&sM[r][16 * j + 4 * g4]) = mk;
-            *reinterpret_cast<bf16x4*>(wA + aq_frag(r, 16 * j + 4 * g4)) = pack_bf16x4(aq);
+            gram_store(3, wave, ck, cq, sBeta[48 + l16]);
         }
         for (int j = wave + 1; j < P::aq_width(wave) / 16; ++j)   // above the diagonal
             *reinterpret_cast<bf16x4*>(wA + aq_frag(r, 16 * j + 4 * g4)) = bf16x4{};
