@@ -41,12 +41,12 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "663abc8fa883f31965b7035830cdd242a82ee0a65c926e9f19ad43774e3cb1b7",
-              86809386, 73925120),
-    "chain": (_PREFILL_SRC, "663abc8fa883f31965b7035830cdd242a82ee0a65c926e9f19ad43774e3cb1b7",
-              125755504, 68203213),
+    "intra": (_PREFILL_SRC, "6844723cfd679f6fd5e16b51e6e92ec427a68cd3f29364ab393cfe08dd2b7fbb",
+              86812042, 73925120),
+    "chain": (_PREFILL_SRC, "6844723cfd679f6fd5e16b51e6e92ec427a68cd3f29364ab393cfe08dd2b7fbb",
+              125760093, 68220518),
     "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
-               547997277, 539214336),
+               547998736, 539222118),
 }
 
 
@@ -123,6 +123,25 @@ def time_calls(fn, steps: int, warmup: int, per_kernel: bool = False):
     return e0.elapsed_time(e1) / steps, wall, stages
 
 
+def call_distribution(fn, steps: int, flush=None):
+    """Times each of `steps` calls on its own, with an event pair around each
+    call (and `flush`, if given, before each pair, outside the events);
+    returns the 10th, 50th and 90th percentiles in microseconds."""
+    import torch
+    begin = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    end = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        begin[i].record()
+        fn(i)
+        end[i].record()
+    torch.cuda.synchronize()
+    t = sorted(b.elapsed_time(e) * 1e3 for b, e in zip(begin, end))
+    pick = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
 def bench_prefill(steps: int, warmup: int):
     import torch
     from gated_delta_rule_42_amd import kda, workloads as wl
@@ -151,7 +170,13 @@ def bench_prefill(steps: int, warmup: int):
     # library's per-kernel events.
     ms, wall, _ = time_calls(call, steps, warmup)
     ms_ev, _, stages = time_calls(call, steps, 0, per_kernel=True)
-    return case, ms, wall, stages, ms_ev
+    # Per-call spread, and the same calls with the 256 MB last-level cache and
+    # the L2s flushed before each one by reading a 512 MiB buffer.
+    spread = {"rotating_inputs": call_distribution(call, steps)}
+    flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    spread["after_512MiB_read_flush"] = call_distribution(call, steps, lambda: flush_buf.sum())
+    del flush_buf
+    return case, ms, wall, stages, ms_ev, spread
 
 
 def bench_decode(steps: int, warmup: int):
@@ -304,7 +329,7 @@ def main() -> int:
     K, W = args.steps, args.warmup
     result = {}
     if args.only in (None, "prefill"):
-        case, ms, wall, stages, ms_ev = bench_prefill(K, W)
+        case, ms, wall, stages, ms_ev, spread = bench_prefill(K, W)
         T, H, d = 4096, 16, 128
         nbytes = prefill_alg_bytes(T, H, d, d, 2, 4, 1)
         stage_bytes = prefill_stage_alg_bytes(T, H, d, d, 2, 4, 1)
@@ -325,6 +350,7 @@ def main() -> int:
                          "traffic": traffic_bytes(dom), "alg_bytes": stage_bytes[dom],
                          "ms_per_launch": stages[dom],
                          "stage_ms": stages, "call_ms_with_kernel_events": ms_ev},
+            "call_us_percentiles": spread,
             "call_roofline": {"kernels": "intra_kernel + chain_kernel", "bound": "hbm",
                               "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": gbs / HBM_PEAK_GBS, "alg_bytes": nbytes,
