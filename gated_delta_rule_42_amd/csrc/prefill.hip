@@ -497,15 +497,20 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     __shared__ __attribute__((aligned(16))) float sBeta[BTP];
     __shared__ __attribute__((aligned(16))) float sCw[CONV ? 3 * kMaxConvWidth * D : 1];   // conv weights
 
-    const int x = blockIdx.x, h = blockIdx.y;
+    // One workgroup per (chunk slot x, head h), heads fastest in the linear
+    // id: workgroups are dealt to the XCDs round-robin by linear id, so
+    // record (x, h) is written on XCD h mod 8 (with H a multiple of 8, the
+    // XCD whose L2 the chain of head h reads from), and the chunks are
+    // dispatched in order.
+    const int x = (int)(blockIdx.x / (unsigned)heads), h = (int)(blockIdx.x % (unsigned)heads);
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, g4 = lane >> 4;
 
     if (wave == 0) {                         // the chain kernel's flags start at zero
         uint32_t* fl = reinterpret_cast<uint32_t*>(ws + flag_off);
-        const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
-        for (int64_t i = ((int64_t)h * gridDim.x + x) * kWave + lane; i < n_flags; i += nwg * kWave) fl[i] = 0;
+        const int64_t nwg = gridDim.x;
+        for (int64_t i = (int64_t)blockIdx.x * kWave + lane; i < n_flags; i += nwg * kWave) fl[i] = 0;
     }
     int seq = 0, first = 0;
     if (!locate_chunk(cu, pos, n_seqs, BT, x, lane, seq, first)) return;
@@ -1495,7 +1500,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 {
     const WorkspaceLayout lay = workspace_layout<D, BT>(a.num_seqs, a.total_tokens, a.heads);
     const int64_t chunks = lay.chunks;
-    if (chunks > INT32_MAX) return hipErrorInvalidValue;
+    if (chunks * a.heads * kThreads > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 1-D intra grid
     const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;
     if (pairs > INT32_MAX) return hipErrorInvalidValue;
     if (a.ev[0]) {
@@ -1512,7 +1517,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         cv.channels = 3 * (int64_t)a.heads * D;
         cv.width = a.conv_width;
         cv.silu = (a.conv_flags & KDA_CONV_SILU) != 0;
-        const dim3 grid((unsigned)chunks, (unsigned)a.heads);
+        const dim3 grid((unsigned)(chunks * a.heads));
         if (a.conv_width > 0)
             hipLaunchKernelGGL((intra_kernel<D, BT, AT, true>), grid, dim3(kThreads), 0, stream,
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
