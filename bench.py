@@ -41,10 +41,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "6844723cfd679f6fd5e16b51e6e92ec427a68cd3f29364ab393cfe08dd2b7fbb",
-              86812042, 73925120),
-    "chain": (_PREFILL_SRC, "6844723cfd679f6fd5e16b51e6e92ec427a68cd3f29364ab393cfe08dd2b7fbb",
-              125760093, 68220518),
+    "intra": (_PREFILL_SRC, "de2bc2d4e06f27eac362a5522186bcb331562a2324c629c86851a4c6785fbf8a",
+              86309443, 73925120),
+    "chain": (_PREFILL_SRC, "de2bc2d4e06f27eac362a5522186bcb331562a2324c629c86851a4c6785fbf8a",
+              125746733, 68245811),
     "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
                547998736, 539222118),
 }
