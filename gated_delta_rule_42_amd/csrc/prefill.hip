@@ -855,8 +855,9 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
             gram_store(wave, j, ck, cq, b_r);
         }
         if (split_gram && wave < 2) {           // block (3, wave)
-            for (int spin = 0; spin < kMaxRowWait &&
-                               __hip_atomic_load(&sRowsReady, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+            int spin = 0;
+            for (; spin < kMaxRowWait &&
+                   __hip_atomic_load(&sRowsReady, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
                  ++spin)
                 __builtin_amdgcn_s_sleep(1);
             f32x4 ck = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
@@ -865,6 +866,10 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                 const bf16x8 a = sKh[wave][kk][lane];
                 ck = mfma16x16x32(a, sKr[0][kk][lane], ck);
                 cq = mfma16x16x32(a, sKr[1][kk][lane], cq);
+            }
+            if (spin == kMaxRowWait) {           // the fragments never came: poison, not garbage
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) ck[ii] = cq[ii] = __builtin_nanf("");
             }
             gram_store(3, wave, ck, cq, sBeta[48 + l16]);
         }
