@@ -41,10 +41,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "de2bc2d4e06f27eac362a5522186bcb331562a2324c629c86851a4c6785fbf8a",
-              86309443, 73925120),
-    "chain": (_PREFILL_SRC, "de2bc2d4e06f27eac362a5522186bcb331562a2324c629c86851a4c6785fbf8a",
-              125746733, 68245811),
+    "intra": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
+              86326867, 73925120),
+    "chain": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
+              125748191, 68271718),
     "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
                547998736, 539222118),
 }
