@@ -7,7 +7,11 @@ Prints ONE JSON line.  The headline `value` is chunk-prefill throughput in
 tokens/s on the single-sequence workload (T=4096, H=16, d_k=d_v=128, C=64,
 bf16 q/k/v, fp32 g/beta, fp32 state in slot 7 of a 64-slot pool), timed over
 exactly K back-to-back calls after W warm-up calls, with torch.cuda.synchronize
-on both sides.  To keep the inputs coming from HBM rather than from the 256 MB
+on both sides.  Before the W warm-up calls each leg runs its calls, untimed,
+for SETTLE_S seconds: a GPU coming out of idle takes tens of milliseconds of
+load to reach its running clocks (measured: ~90 µs per prefill call after 10
+warm-up calls from idle, ~82 µs after 200), so a short warm-up would time the
+ramp rather than the kernels.  To keep the inputs coming from HBM rather than from the 256 MB
 last-level cache, the calls rotate over four independent copies of the
 activations (each ~80 MB).  The same line carries:
   * decode: seq/s for 512 sequences x 1 token on an fp32 pool of 1024 slots;
@@ -42,11 +46,11 @@ _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
     "intra": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
-              86326867, 73925120),
+              86324362, 73925120),
     "chain": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
-              125748191, 68271718),
+              125747490, 68158976),
     "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
-               547998736, 539222118),
+               547990692, 539236557),
 }
 
 
@@ -95,13 +99,29 @@ def decode_alg_bytes(B: int, H: int, dk: int, dv: int, act_bytes: int, state_byt
     return B * H * per_seq_head
 
 
+SETTLE_S = 0.25
+
+
+def settle(fn, seconds: float = SETTLE_S) -> None:
+    """Runs fn untimed for about `seconds` of GPU time (in batches of 20 calls
+    with a synchronize after each), so the GPU is at its running clocks."""
+    import torch
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_calls(fn, steps: int, warmup: int, per_kernel: bool = False):
-    """Warm up, then time exactly `steps` calls with HIP events on the current
-    stream (the stream the kernels run on), bracketed by synchronize.  With
-    per_kernel, the library's prefill timing session also records events
+    """Settle, warm up, then time exactly `steps` calls with HIP events on the
+    current stream (the stream the kernels run on), bracketed by synchronize.
+    With per_kernel, the library's prefill timing session also records events
     around each of its two kernels inside the same timed region."""
     import torch
     from gated_delta_rule_42_amd import kda
+    settle(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
