@@ -137,7 +137,11 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *               such a pair on different XCDs, that tile's output rows come out
  *               NaN (never stale values).
  * States are computed in fp32 between chunks; a bf16 state is rounded to
- * nearest-even when stored (final state and checkpoints).
+ * nearest-even when stored (final state and checkpoints).  A call with more
+ * than 2^24 (chunk slot, head) pairs -- chunk slots being
+ * ceil(total_tokens / chunk_size) + 2 * num_seqs -- does not fit the
+ * one-dimensional grid of the first kernel and returns KDA_ERR_LAUNCH
+ * without enqueuing anything.
  */
 kda_status_t kda_chunk_prefill(
     const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
