@@ -110,6 +110,9 @@ def test_prefill_validation(lib):
     assert _prefill(lib, interval=64, cap=4, ck=None) == K.KDA_ERR_INVALID_ARG
     assert _prefill(lib, T=-1) == K.KDA_ERR_INVALID_ARG
     assert _prefill(lib, wsb=100) == K.KDA_ERR_WORKSPACE_TOO_SMALL
+    # 2^20 + 2 chunk slots x 16 heads exceeds the first kernel's 1-D grid:
+    # refused on the host, before anything is enqueued (no GPU needed).
+    assert _prefill(lib, T=1 << 26, wsb=1 << 62) == K.KDA_ERR_LAUNCH
     need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
     assert _prefill(lib, wsb=need, ws=FAKE + 16) == K.KDA_ERR_INVALID_ARG   # 256-B alignment
 
