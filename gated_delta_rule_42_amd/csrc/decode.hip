@@ -34,9 +34,10 @@ template <int DK, int DV>
 struct DecodeShape {
     static constexpr int CPT = 4;                                    // columns per thread
     static constexpr int TPR = DV / CPT;                             // threads per row
-    static constexpr int RG = (DK < 512 / TPR) ? DK : 512 / TPR;     // row groups
+    static constexpr int RG = (DK < 1024 / TPR) ? DK : 1024 / TPR;   // row groups
     static constexpr int NT = TPR * RG;                              // block size
     static constexpr int RPT = DK / RG;                              // rows per thread
+    static_assert(CPT == 4, "each thread moves one 4-column vector per row");
     static_assert(DV % CPT == 0 && DK % RG == 0 && NT % kWave == 0, "decode shape");
 };
 
