@@ -48,9 +48,9 @@ MEASURED_TRAFFIC = {
     "intra": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
               86324362, 73925120),
     "chain": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
-              125747490, 68158976),
-    "decode": (_DECODE_SRC, "1a222fbb779bfa890e2e1bb28c61c13bb87ce44d51f2e63e8650e74cd87dbe1d",
-               547990692, 539236557),
+              125747490, 68159078),
+    "decode": (_DECODE_SRC, "1901e51721b477cbeb63fad8f599d29b1abd0a826a040501bd556f1b7d6b84e3",
+               547988644, 539490202),
 }
 
 
