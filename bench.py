@@ -49,8 +49,8 @@ MEASURED_TRAFFIC = {
               86324362, 73925120),
     "chain": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
               125747490, 68159078),
-    "decode": (_DECODE_SRC, "1901e51721b477cbeb63fad8f599d29b1abd0a826a040501bd556f1b7d6b84e3",
-               547988644, 539490202),
+    "decode": (_DECODE_SRC, "34ff4d70888795f19b3e3393ea60a9432125b3a712f0404aca95d57dc214505c",
+               547988644, 539478221),
 }
 
 

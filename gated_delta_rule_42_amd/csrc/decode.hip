@@ -181,8 +181,12 @@ void kda_decode_kernel(const AT* __restrict__ q, const AT* __restrict__ k,
 
 // Commit of a speculative step: pool[slot_b] = token_states[b, n_b - 1] for
 // 0 < n_b <= ntok.  One workgroup per (row, head), a streaming copy.
+// 1024 threads: 512 rows x 16 heads of 128 x 128 fp32 states commit in
+// 154.7 us on MI355X (166 us with 256 threads, 159 with 512).
+constexpr int kCommitThreads = 1024;
+
 template <typename ST>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(kCommitThreads)
 void kda_spec_commit_kernel(const ST* __restrict__ token_states, int heads, int ntok, int64_t elems,
                             const int32_t* __restrict__ accepted, ST* __restrict__ pool,
                             int64_t num_slots, const int32_t* __restrict__ slots)
@@ -193,7 +197,7 @@ void kda_spec_commit_kernel(const ST* __restrict__ token_states, int heads, int 
     if (slot < 0 || slot >= num_slots || n <= 0 || n > ntok) return;
     const ST* src = token_states + (((int64_t)b * ntok + n - 1) * heads + h) * elems;
     ST* dstp = pool + ((int64_t)slot * heads + h) * elems;
-    for (int64_t i = 4 * (int64_t)threadIdx.x; i < elems; i += 4 * 256) {
+    for (int64_t i = 4 * (int64_t)threadIdx.x; i < elems; i += 4 * kCommitThreads) {
         float x[4];
         load4_stream(src + i, x);
         store4_stream(dstp + i, x);
@@ -229,7 +233,7 @@ hipError_t launch_dim(const DecodeArgs& a, hipStream_t stream)
 hipError_t launch_spec_commit(const SpecCommitArgs& a, hipStream_t stream)
 {
     const int64_t elems = (int64_t)a.dk * a.dv;
-    dim3 grid((unsigned)((int64_t)a.batch * a.heads)), block(256);
+    dim3 grid((unsigned)((int64_t)a.batch * a.heads)), block(kCommitThreads);
     if (a.state == KDA_BF16)
         hipLaunchKernelGGL((kda_spec_commit_kernel<bf16>), grid, block, 0, stream,
                            static_cast<const bf16*>(a.token_states), a.heads, a.ntok, elems,
