@@ -45,10 +45,8 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
-              86324362, 73925120),
-    "chain": (_PREFILL_SRC, "358cd4a205485235c26640db0aed9d44bf50af181969b8738920429fb1d28545",
-              125747490, 68159078),
+    "intra": (_PREFILL_SRC, "", 0, 0),
+    "chain": (_PREFILL_SRC, "", 0, 0),
     "decode": (_DECODE_SRC, "34ff4d70888795f19b3e3393ea60a9432125b3a712f0404aca95d57dc214505c",
                547988644, 539478221),
 }
@@ -58,6 +56,20 @@ def source_sha256(rel: str) -> str:
     import hashlib
     with open(os.path.join(ROOT, rel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
+
+
+# Per-kernel durations of one prefill call from the committed rocprofv3
+# kernel-trace summary of this bench's prefill leg (source, its sha256 when
+# profiled, {kernel: mean µs}): the split of the call, valid only for the
+# source it was measured on.
+PROFILE_SPLIT = (_PREFILL_SRC, "", "profiles/prefill_T4096_H16_d128_kernel_trace.md", {})
+
+
+def profile_split():
+    src, sha, path, split = PROFILE_SPLIT
+    if not split or sha != source_sha256(src):
+        return None
+    return {"source": path, "mean_us": split}
 
 
 def traffic_bytes(kernel: str):
@@ -83,17 +95,6 @@ def prefill_alg_flops(T: int, H: int, d: int, C: int) -> float:
     return per_chunk / C * T * H
 
 
-def prefill_stage_alg_bytes(T: int, H: int, dk: int, dv: int, act_bytes: int, state_bytes: int,
-                            n_states: int) -> dict:
-    """The same algorithmic bytes split by the kernel that must move them: the
-    intra-chunk kernel reads q, k, v, g and beta; the chain kernel reads and
-    writes the states and writes o.  The workspace records passed from one to
-    the other are an artefact of the split, not algorithmic traffic."""
-    intra = T * H * ((2 * dk + dv) * act_bytes + 4 * dk + 4)
-    chain = T * H * dv * act_bytes + 2 * n_states * H * dk * dv * state_bytes
-    return {"intra": intra, "chain": chain}
-
-
 def decode_alg_bytes(B: int, H: int, dk: int, dv: int, act_bytes: int, state_bytes: int) -> int:
     per_seq_head = 2 * dk * dv * state_bytes + (2 * dk + 2 * dv) * act_bytes + 4 * dk + 4
     return B * H * per_seq_head
@@ -114,21 +115,16 @@ def settle(fn, seconds: float = SETTLE_S) -> None:
         torch.cuda.synchronize()
 
 
-def time_calls(fn, steps: int, warmup: int, per_kernel: bool = False):
+def time_calls(fn, steps: int, warmup: int):
     """Settle, warm up, then time exactly `steps` calls with HIP events on the
-    current stream (the stream the kernels run on), bracketed by synchronize.
-    With per_kernel, the library's prefill timing session also records events
-    around each of its two kernels inside the same timed region."""
+    current stream (the stream the kernels run on), bracketed by synchronize."""
     import torch
-    from gated_delta_rule_42_amd import kda
     settle(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    if per_kernel:
-        kda.prefill_timing_begin(steps)
     w0 = time.perf_counter()
     e0.record()
     for i in range(steps):
@@ -136,11 +132,7 @@ def time_calls(fn, steps: int, warmup: int, per_kernel: bool = False):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    stages = None
-    if per_kernel:
-        intra_ms, chain_ms, n = kda.prefill_timing_end()
-        stages = {"intra": intra_ms / n, "chain": chain_ms / n}
-    return e0.elapsed_time(e1) / steps, wall, stages
+    return e0.elapsed_time(e1) / steps, wall
 
 
 def call_distribution(fn, steps: int, flush=None):
@@ -184,19 +176,17 @@ def bench_prefill(steps: int, warmup: int):
         q, k, v, g, beta = sets[i % n_sets]
         kda.chunk_prefill(q, k, v, g, beta, cu, pool, slots, out, workspace=ws, chunk_size=64)
 
-    # The call rate comes from a timed region with no events between the two
-    # kernels (an event record there costs the call several µs); the kernel
-    # durations come from a second timed region of the same length with the
-    # library's per-kernel events.
-    ms, wall, _ = time_calls(call, steps, warmup)
-    ms_ev, _, stages = time_calls(call, steps, 0, per_kernel=True)
+    ms, wall = time_calls(call, steps, warmup)
     # Per-call spread, and the same calls with the 256 MB last-level cache and
     # the L2s flushed before each one by reading a 512 MiB buffer.
     spread = {"rotating_inputs": call_distribution(call, steps)}
     flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     spread["after_512MiB_read_flush"] = call_distribution(call, steps, lambda: flush_buf.sum())
     del flush_buf
-    return case, ms, wall, stages, ms_ev, spread
+    status = kda.chunk_prefill_check(ws)
+    if status != 0:
+        raise RuntimeError(f"prefill reported device status {status:#x}")
+    return case, ms, wall, spread
 
 
 def bench_decode(steps: int, warmup: int):
@@ -212,7 +202,7 @@ def bench_decode(steps: int, warmup: int):
     def call(i):
         kda.recurrent_decode(q, k, v, g, beta, pool, slots, out)
 
-    ms, wall, _ = time_calls(call, steps, warmup)
+    ms, wall = time_calls(call, steps, warmup)
     return case, ms, wall
 
 
@@ -240,13 +230,13 @@ def bench_spec(steps: int, warmup: int):
     def call(i):
         kda.spec_decode(q, k, v, g, beta, pool, slots, ts, out)
 
-    ms, wall, _ = time_calls(call, steps, warmup)
+    ms, wall = time_calls(call, steps, warmup)
     acc = case.accepted.to(dev)
 
     def commit(i):
         kda.spec_commit(ts, acc, pool, slots)
 
-    cms, _, _ = time_calls(commit, steps, warmup)
+    cms, _ = time_calls(commit, steps, warmup)
     return case, ms, cms
 
 
@@ -287,8 +277,8 @@ def bench_pipeline(steps: int, warmup: int):
                                flags=kda.KDA_FLAG_QK_L2NORM)
         kda.gated_rmsnorm(o, gate, z, weight=nw, eps=lc.eps)
 
-    ums, _, _ = time_calls(unfused, steps, warmup)
-    ms, wall, _ = time_calls(fused, steps, warmup)
+    ums, _ = time_calls(unfused, steps, warmup)
+    ms, wall = time_calls(fused, steps, warmup)
     return lc, ms, wall, ums
 
 
@@ -299,7 +289,7 @@ def bench_copy(steps: int, warmup: int, nbytes: int = 1 << 30):
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    ms, wall, _ = time_calls(lambda i: dst.copy_(src), steps, warmup)
+    ms, wall = time_calls(lambda i: dst.copy_(src), steps, warmup)
     return {"value": 2 * nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s (read + write)",
             "ms_per_step": ms, "steps": steps, "bytes_read": nbytes, "bytes_written": nbytes}
 
@@ -320,8 +310,14 @@ def cpu_baseline(case, budget_s: float = 10.0):
         if el >= budget_s:
             break
     units = case.num_seqs * case.q.shape[1]
+    host = os.cpu_count()
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = host
     return {"value": case.total_tokens * reps / el, "unit": "tokens/s",
-            "cores": min(oracle.num_threads(), units), "kind": "oracle",
+            "cores": min(oracle.num_threads(), units), "host_cores": host,
+            "host_cores_usable": usable, "kind": "oracle",
             "sample": f"full prefill workload (T={case.total_tokens}, H={case.q.shape[1]}, "
                       f"d=128) x{reps} calls in {el:.1f} s; OpenMP over the {units} "
                       f"(sequence, head) units"}
@@ -349,14 +345,18 @@ def main() -> int:
     K, W = args.steps, args.warmup
     result = {}
     if args.only in (None, "prefill"):
-        case, ms, wall, stages, ms_ev, spread = bench_prefill(K, W)
+        case, ms, wall, spread = bench_prefill(K, W)
         T, H, d = 4096, 16, 128
         nbytes = prefill_alg_bytes(T, H, d, d, 2, 4, 1)
-        stage_bytes = prefill_stage_alg_bytes(T, H, d, d, 2, 4, 1)
         flops = prefill_alg_flops(T, H, d, 64)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        dom = max(stages, key=stages.get)
-        dom_gbs = stage_bytes[dom] / (stages[dom] * 1e-3) / 1e9
+        tflops = flops / (ms * 1e-3) / 1e12
+        # Fraction of the binding roofline of the call: the longer of the
+        # HBM time of its algorithmic bytes and the MFMA time of its
+        # algorithmic flops, over the measured time.
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
         result.update({
             "metric": "KDA prefill tokens/s (T=4096,H=16,d=128) + decode seq/s; % MFMA/HBM roofline",
             "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -365,17 +365,21 @@ def main() -> int:
             "config": {"workload": case.name, "seqs": 1, "seq_len": T, "heads": H, "d_k": d,
                        "d_v": d, "chunk": 64, "act": "bf16", "g_beta": "fp32",
                        "state": "fp32 pool[64] slot 7", "parallelism": "none (1 GPU)"},
-            "roofline": {"kernel": f"{dom}_kernel", "bound": "hbm", "achieved": dom_gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                         "traffic": traffic_bytes(dom), "alg_bytes": stage_bytes[dom],
-                         "ms_per_launch": stages[dom],
-                         "stage_ms": stages, "call_ms_with_kernel_events": ms_ev},
+            "roofline": {"kernel": "whole prefill call (flag-clearing kernel, intra_kernel, "
+                                   "chain_kernel); the time is the call's",
+                         "bound": bound,
+                         "achieved": gbs if bound == "hbm" else tflops,
+                         "peak": HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS,
+                         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                         "frac": max(t_hbm, t_mfma) / (ms * 1e-3),
+                         "traffic": (None if None in (traffic_bytes("intra"), traffic_bytes("chain"))
+                                     else traffic_bytes("intra") + traffic_bytes("chain")),
+                         "alg_bytes": nbytes,
+                         "alg_flops": flops, "ms_per_launch": ms,
+                         "hbm_frac": gbs / HBM_PEAK_GBS,
+                         "mfma_frac_algorithmic": tflops / BF16_PEAK_TFLOPS,
+                         "kernel_split": profile_split()},
             "call_us_percentiles": spread,
-            "call_roofline": {"kernels": "intra_kernel + chain_kernel", "bound": "hbm",
-                              "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": gbs / HBM_PEAK_GBS, "alg_bytes": nbytes,
-                              "alg_flops": flops,
-                              "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         })
     if args.only in (None, "decode"):
         dcase, dms, dwall = bench_decode(K, W)

@@ -24,6 +24,8 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # Keep the compiler from forming packed-fp32 instructions.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # Export only the entry points that kda.h marks KDA_API.
+         "-fvisibility=hidden",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -21,7 +21,7 @@
 //                 old rows it needs before writing, so no thread overwrites a
 //                 row another still reads.
 
-#include "kda_device.cuh"
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {

@@ -24,7 +24,7 @@
 // column reductions (u, w) are summed inside each thread over its rows, then
 // across row groups through LDS in a fixed order (deterministic).
 
-#include "kda_device.cuh"
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {

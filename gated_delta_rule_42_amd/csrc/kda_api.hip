@@ -20,21 +20,6 @@ kda_status_t launch_status(hipError_t e)
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-// Prefill timing session: 3 events per call, created at begin.
-struct TimingSession {
-    hipEvent_t* events = nullptr;
-    int32_t capacity = 0;
-    int32_t used = 0;
-};
-TimingSession g_timing;
-
-void destroy_events(hipEvent_t* ev, int32_t n)
-{
-    for (int32_t i = 0; i < n; ++i)
-        if (ev[i]) (void)hipEventDestroy(ev[i]);
-    delete[] ev;
-}
-
 }  // namespace
 
 extern "C" {
@@ -49,6 +34,7 @@ const char* kda_status_string(kda_status_t status)
         case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype, chunk size or interval";
         case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KDA_ERR_LAUNCH: return "kernel launch failed";
+        case KDA_ERR_DEVICE: return "the device reported a failed call";
         default: return "unknown status";
     }
 }
@@ -122,11 +108,6 @@ kda_status_t prefill_common(
     a.seq_pos = nullptr;
     a.conv_w = a.conv_b = nullptr; a.conv_state = nullptr;
     a.conv_width = 0; a.conv_flags = 0;
-    a.ev[0] = a.ev[1] = a.ev[2] = nullptr;
-    if (g_timing.events && g_timing.used < g_timing.capacity) {
-        hipEvent_t* ev = g_timing.events + 3 * g_timing.used++;
-        a.ev[0] = ev[0]; a.ev[1] = ev[1]; a.ev[2] = ev[2];
-    }
     return KDA_OK;
 }
 
@@ -153,6 +134,19 @@ kda_status_t kda_chunk_prefill(
         out_stride_t, workspace, workspace_bytes);
     if (st != KDA_OK || num_seqs == 0) return st;
     return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_chunk_prefill_check(const void* workspace, size_t workspace_bytes,
+                                     uint32_t* device_flags, void* stream)
+{
+    if (!workspace || workspace_bytes < 4) return KDA_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    if (hipStreamSynchronize(s) != hipSuccess) return KDA_ERR_LAUNCH;
+    if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        return KDA_ERR_LAUNCH;
+    if (device_flags) *device_flags = word;
+    return word == 0 ? KDA_OK : KDA_ERR_DEVICE;
 }
 
 kda_status_t kda_chunk_prefill_at(
@@ -217,48 +211,6 @@ kda_status_t kda_conv_chunk_prefill(
     a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state_pool;
     a.conv_width = conv_width; a.conv_flags = conv_flags;
     return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
-}
-
-kda_status_t kda_prefill_timing_begin(int32_t max_calls)
-{
-    if (max_calls <= 0 || max_calls > (1 << 20) || g_timing.events) return KDA_ERR_INVALID_ARG;
-    const int32_t n = 3 * max_calls;
-    hipEvent_t* ev = new hipEvent_t[n]();
-    for (int32_t i = 0; i < n; ++i) {
-        if (hipEventCreate(&ev[i]) != hipSuccess) {
-            destroy_events(ev, n);
-            return KDA_ERR_LAUNCH;
-        }
-    }
-    g_timing.events = ev;
-    g_timing.capacity = max_calls;
-    g_timing.used = 0;
-    return KDA_OK;
-}
-
-kda_status_t kda_prefill_timing_end(float* stage_ms, int32_t* calls)
-{
-    if (!g_timing.events || !stage_ms || !calls) return KDA_ERR_INVALID_ARG;
-    kda_status_t st = KDA_OK;
-    double sum[2] = {0.0, 0.0};
-    for (int32_t c = 0; c < g_timing.used && st == KDA_OK; ++c) {
-        hipEvent_t* ev = g_timing.events + 3 * c;
-        if (hipEventSynchronize(ev[2]) != hipSuccess) { st = KDA_ERR_LAUNCH; break; }
-        for (int s = 0; s < 2; ++s) {
-            float ms = 0.f;
-            if (hipEventElapsedTime(&ms, ev[s], ev[s + 1]) != hipSuccess) {
-                st = KDA_ERR_LAUNCH;
-                break;
-            }
-            sum[s] += ms;
-        }
-    }
-    stage_ms[0] = (float)sum[0];
-    stage_ms[1] = (float)sum[1];
-    *calls = g_timing.used;
-    destroy_events(g_timing.events, 3 * g_timing.capacity);
-    g_timing = TimingSession();
-    return st;
 }
 
 kda_status_t kda_recurrent_decode(

@@ -1,4 +1,4 @@
-// kda_device.cuh -- device helpers shared by the KDA kernels (gfx950, wave64).
+// kda_device.h -- device helpers shared by the KDA kernels (gfx950, wave64).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -59,10 +59,6 @@ struct PrefillArgs {
     // pool is indexed like the state pool (same slots, has_init, num_slots).
     const void* conv_w; const void* conv_b; void* conv_state;
     int32_t conv_width; uint32_t conv_flags;
-    // Optional timing events (all null, or all valid): recorded on the stream
-    // before the intra-chunk kernel, between it and the chain kernel, and
-    // after the chain kernel.
-    hipEvent_t ev[3];
 };
 // Workspace bytes for a call; 0 if the shape is unsupported.
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t heads,

@@ -17,7 +17,7 @@
 // shuffles in a fixed order, so results are deterministic.  x (and the
 // residual) are read a second time after the reduction, from the cache.
 
-#include "kda_device.cuh"
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {

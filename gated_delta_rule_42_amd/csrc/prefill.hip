@@ -39,9 +39,10 @@
 // Off-diagonal blocks have both factors <= 1; diagonal blocks grow at most by
 // the decay accumulated inside one sub-chunk, which must stay above e^{-80}.
 
+#include <algorithm>
 #include <type_traits>
 
-#include "kda_device.cuh"
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -55,6 +56,17 @@ constexpr float kMaxLogDecay = 80.0f;
 // Bound on a wave's wait for another wave of its workgroup (that wave writes
 // within a few hundred cycles; the bound only keeps every wait finite).
 constexpr int kMaxRowWait = 1 << 20;
+// The workspace starts with a header whose first word is the call's status:
+// a bounded wait that ran out sets a bit in it (its results are then NaN, not
+// stale values), and the host reads it back on request.  The kernels get the
+// rest of the workspace, past the header.
+constexpr int64_t kHeaderBytes = 256;
+constexpr uint32_t kStatusTimeout = 1u;     // a bounded wait ran out
+constexpr uint32_t kStatusPlacement = 2u;   // the two workgroups of a tile ran on different XCDs
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits)
+{
+    __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int D, int BT>
 struct Shape {
@@ -458,8 +470,8 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                   int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ g,
                   const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
                   int heads, const int32_t* __restrict__ slots, uint32_t flags,
-                  const int64_t* __restrict__ pos, uint8_t* __restrict__ ws, int64_t flag_off,
-                  int64_t n_flags, ConvIn<AT> cv)
+                  const int64_t* __restrict__ pos, uint8_t* __restrict__ ws,
+                  uint32_t* __restrict__ status, ConvIn<AT> cv)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NKK = P::NKK_K;
@@ -507,11 +519,6 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    if (wave == 0) {                         // the chain kernel's flags start at zero
-        uint32_t* fl = reinterpret_cast<uint32_t*>(ws + flag_off);
-        const int64_t nwg = gridDim.x;
-        for (int64_t i = (int64_t)blockIdx.x * kWave + lane; i < n_flags; i += nwg * kWave) fl[i] = 0;
-    }
     int seq = 0, first = 0;
     if (!locate_chunk(cu, pos, n_seqs, BT, x, lane, seq, first)) return;
     if (slots[seq] < 0) return;              // padding sequence: nothing to precompute
@@ -870,6 +877,7 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
             if (spin == kMaxRowWait) {           // the fragments never came: poison, not garbage
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) ck[ii] = cq[ii] = __builtin_nanf("");
+                raise_status(status, kStatusTimeout);
             }
             gram_store(3, wave, ck, cq, sBeta[48 + l16]);
         }
@@ -1135,7 +1143,8 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                   ST* __restrict__ pool, int64_t num_slots, const int32_t* __restrict__ slots,
                   const uint8_t* __restrict__ has_init, ST* __restrict__ ckpt, int64_t ckpt_cap,
                   int interval, float scale, AT* __restrict__ out, int64_t os,
-                  uint8_t* __restrict__ ws, int64_t xch_off, int64_t xch_chunks, int64_t flag_off)
+                  uint8_t* __restrict__ ws, int64_t xch_off, int64_t xch_chunks, int64_t flag_off,
+                  uint32_t* __restrict__ status)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NB = kChainBufs;
@@ -1292,8 +1301,8 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
         };
         // Publishes that chunks 0 .. n - 1 are in their exchange slots.
         auto publish = [&](int n) {
-            if (wave == 0 && lane == 0)
-                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (wave == 0)
+                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
         auto step = [&](int lc, const Ops& o, auto refill) {
             uint8_t* const slot_x = xch + (int64_t)lc * XSLOT;
@@ -1389,14 +1398,18 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
         bool broken = false;
         auto wait_chunk = [&](int c) {             // until chunk c is published
             if (broken) return;
+            uint32_t f = 0;
             for (int spin = 0; spin < kMaxSpin; ++spin) {
                 // Polled with device-scope atomic loads: a plain load can keep
                 // hitting the CU's own cached copy of the flag.
-                const uint32_t f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if ((f >> 24) == xcc && (f & 0xffffff) > (uint32_t)c) return;
                 __builtin_amdgcn_s_sleep(2);
             }
+            // A flag carrying another XCD's id: the pair was split across
+            // XCDs; otherwise the producer never got this far.
             broken = true;
+            raise_status(status, f != 0 && (f >> 24) != xcc ? kStatusPlacement : kStatusTimeout);
         };
         auto copy = [&](int c) {                   // 1 KB pieces, device-coherent at L2
             const uint8_t* src = xch + (int64_t)min(c, nch - 1) * XSLOT;
@@ -1480,9 +1493,20 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     run_steps<NB>(nch, buf, fetch, step);
 }
 
+// Clears the status word and the chain kernel's flags before a call's
+// kernels run (a kernel, not a memset, so the call can be graph-captured).
+__global__ __launch_bounds__(kThreads)
+void prefill_reset_kernel(uint32_t* __restrict__ status, uint32_t* __restrict__ flags, int64_t n_flags)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_flags; i += (int64_t)gridDim.x * kThreads)
+        flags[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
-// Workspace: the records, then the chain's exchange slots (per head and
-// column tile, one per chunk slot), then one flag per (sequence, head, tile).
+// Workspace, past the header: the records, then the chain's exchange slots
+// (per head and column tile, one per chunk slot), then one flag per
+// (sequence, head, tile).
 struct WorkspaceLayout {
     int64_t chunks, xch_off, flag_off, n_flags, bytes;
 };
@@ -1496,7 +1520,7 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t total_tokens, int32_t
     l.xch_off = l.chunks * heads * P::REC_BYTES;
     l.flag_off = l.xch_off + (int64_t)heads * (D / 16) * l.chunks * xslot;
     l.n_flags = (int64_t)num_seqs * heads * (D / 16);
-    l.bytes = l.flag_off + (l.n_flags * 4 + 255) / 256 * 256;
+    l.bytes = kHeaderBytes + l.flag_off + (l.n_flags * 4 + 255) / 256 * 256;
     return l;
 }
 
@@ -1508,8 +1532,13 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     if (chunks * a.heads * kThreads > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 1-D intra grid
     const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;
     if (pairs > INT32_MAX) return hipErrorInvalidValue;
-    if (a.ev[0]) {
-        const hipError_t e = hipEventRecord(a.ev[0], stream);
+    uint32_t* const status = static_cast<uint32_t*>(a.workspace);
+    uint8_t* const ws = static_cast<uint8_t*>(a.workspace) + kHeaderBytes;
+    {
+        const unsigned blocks = (unsigned)std::min<int64_t>(64, (lay.n_flags + kThreads - 1) / kThreads + 1);
+        hipLaunchKernelGGL(prefill_reset_kernel, dim3(blocks), dim3(kThreads), 0, stream, status,
+                           reinterpret_cast<uint32_t*>(ws + lay.flag_off), lay.n_flags);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (a.total_tokens > 0) {
@@ -1528,31 +1557,23 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               a.seq_pos, static_cast<uint8_t*>(a.workspace), lay.flag_off,
-                               lay.n_flags, cv);
+                               a.seq_pos, ws, status, cv);
         else
             hipLaunchKernelGGL((intra_kernel<D, BT, AT, false>), grid, dim3(kThreads), 0, stream,
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               a.seq_pos, static_cast<uint8_t*>(a.workspace), lay.flag_off,
-                               lay.n_flags, cv);
+                               a.seq_pos, ws, status, cv);
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (a.ev[1]) {
-        const hipError_t e = hipEventRecord(a.ev[1], stream);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST>), dim3((unsigned)pairs, (unsigned)(D / 16), 2u),
                        dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                        static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                        static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
-                       static_cast<AT*>(a.out), a.out_stride, static_cast<uint8_t*>(a.workspace),
-                       lay.xch_off, lay.chunks, lay.flag_off);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !a.ev[2]) return e;
-    return hipEventRecord(a.ev[2], stream);
+                       static_cast<AT*>(a.out), a.out_stride, ws,
+                       lay.xch_off, lay.chunks, lay.flag_off, status);
+    return hipGetLastError();
 }
 
 template <int D, int BT>

@@ -20,6 +20,7 @@ KDA_ERR_INVALID_ARG = 1
 KDA_ERR_UNSUPPORTED = 2
 KDA_ERR_WORKSPACE_TOO_SMALL = 3
 KDA_ERR_LAUNCH = 4
+KDA_ERR_DEVICE = 5
 
 KDA_F32 = 0
 KDA_BF16 = 1
@@ -90,11 +91,8 @@ def _load() -> ctypes.CDLL:
         vp, i32, i64, vp, vp, f32, u32, vp, i64, vp]
     lib.kda_spec_commit.restype = i32
     lib.kda_spec_commit.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i32, i64, vp, vp]
-    lib.kda_prefill_timing_begin.restype = i32
-    lib.kda_prefill_timing_begin.argtypes = [i32]
-    lib.kda_prefill_timing_end.restype = i32
-    lib.kda_prefill_timing_end.argtypes = [ctypes.POINTER(ctypes.c_float),
-                                           ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_chunk_prefill_check.restype = i32
+    lib.kda_chunk_prefill_check.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_uint32), vp]
     return lib
 
 
@@ -396,16 +394,13 @@ def causal_conv1d(x, weight, cu_seqlens, conv_state_pool, state_indices, y, *, b
     _check("kda_causal_conv1d", status)
 
 
-def prefill_timing_begin(max_calls: int) -> None:
-    """kda_prefill_timing_begin: time the two kernels of the next `max_calls`
-    chunk_prefill calls with HIP events on their stream."""
-    _check("kda_prefill_timing_begin", _lib.kda_prefill_timing_begin(int(max_calls)))
-
-
-def prefill_timing_end() -> tuple[float, float, int]:
-    """kda_prefill_timing_end: (intra-chunk ms, chain ms) summed over the timed
-    calls, and the number of calls timed."""
-    ms = (ctypes.c_float * 2)()
-    n = ctypes.c_int32(0)
-    _check("kda_prefill_timing_end", _lib.kda_prefill_timing_end(ms, ctypes.byref(n)))
-    return float(ms[0]), float(ms[1]), int(n.value)
+def chunk_prefill_check(workspace, *, stream=None) -> int:
+    """kda_chunk_prefill_check: waits for the stream and returns the status
+    word the last prefill call on `workspace` left (0 = the call completed
+    normally).  Synchronises; a diagnostic, not for the hot path."""
+    word = ctypes.c_uint32(0)
+    status = _lib.kda_chunk_prefill_check(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          ctypes.byref(word), _stream(stream))
+    if status not in (KDA_OK, KDA_ERR_DEVICE):
+        _check("kda_chunk_prefill_check", status)
+    return int(word.value)

@@ -15,12 +15,12 @@
  *
  * Conventions for every entry point
  *   - Every pointer argument is DEVICE memory owned by the caller, except
- *     where a comment says otherwise.  Apart from the optional timing aid at the
- *     end of this header, the library allocates nothing, keeps no state
- *     between calls and never synchronises: each call only enqueues
- *     kernels on `stream` (a hipStream_t; NULL = the null stream), so it can
- *     be captured into a HIP graph.  Outputs are valid once the stream has
- *     reached that point.
+ *     where a comment says otherwise.  The library allocates nothing and
+ *     keeps no state between calls.  Apart from kda_chunk_prefill_check (a
+ *     diagnostic that waits for its stream) no call synchronises: each only
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream),
+ *     so it can be captured into a HIP graph.  Outputs are valid once the
+ *     stream has reached that point.
  *   - Layouts are row-major.  Activations are [tokens, heads, dim] with the
  *     head blocks of one token contiguous and a caller-given token stride (in
  *     elements), so packed projections can be read in place.  Recurrent
@@ -50,6 +50,10 @@ extern "C" {
 
 #define KDA_ABI_VERSION 1
 
+/* The library is built with hidden symbol visibility: exactly the entry
+ * points declared here are exported. */
+#define KDA_API __attribute__((visibility("default")))
+
 /* Status codes. */
 typedef int32_t kda_status_t;
 #define KDA_OK 0
@@ -57,6 +61,7 @@ typedef int32_t kda_status_t;
 #define KDA_ERR_UNSUPPORTED 2          /* dims / chunk size / dtype / interval not built */
 #define KDA_ERR_WORKSPACE_TOO_SMALL 3  /* workspace_bytes below the query's result     */
 #define KDA_ERR_LAUNCH 4               /* hipGetLastError() after the launch            */
+#define KDA_ERR_DEVICE 5               /* kda_chunk_prefill_check: the device reported a failure */
 
 /* Element types. */
 typedef int32_t kda_dtype_t;
@@ -73,10 +78,10 @@ typedef int32_t kda_dtype_t;
 /* Supported shapes: d_k = d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64}. */
 
 /* KDA_ABI_VERSION of the loaded library. */
-int kda_abi_version(void);
+KDA_API int kda_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
-const char* kda_status_string(kda_status_t status);
+KDA_API const char* kda_status_string(kda_status_t status);
 
 /*
  * Bytes of caller-owned scratch that kda_chunk_prefill needs for a call with
@@ -85,7 +90,7 @@ const char* kda_status_string(kda_status_t status);
  * buffer sized for the largest batch serves every later call.  Returns 0 for
  * unsupported shapes.
  */
-size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
+KDA_API size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                         int32_t num_heads, int32_t dk, int32_t dv,
                                         int32_t chunk_size);
 
@@ -131,19 +136,28 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *               sequence are left alone.
  *   workspace   at least kda_chunk_prefill_workspace_size(...) bytes, 256-byte
  *               aligned.  Its contents are scratch: any call may overwrite it,
- *               so concurrent calls need separate workspaces.  It also carries
- *               the per-chunk exchange between the two workgroups that share
- *               each 16-column tile of the state; should the GPU ever place
- *               such a pair on different XCDs, that tile's output rows come out
- *               NaN (never stale values).
+ *               so concurrent calls need separate workspaces.  Its first 4
+ *               bytes are a status word that kda_chunk_prefill_check reads.
+ *               It also carries the per-chunk exchange between the two
+ *               workgroups that share each 16-column tile of the state;
+ *               should the GPU ever place such a pair on different XCDs, that
+ *               tile's output rows come out NaN (never stale values) and the
+ *               status word says so.
  * States are computed in fp32 between chunks; a bf16 state is rounded to
- * nearest-even when stored (final state and checkpoints).  A call with more
- * than 2^24 (chunk slot, head) pairs -- chunk slots being
+ * nearest-even when stored (final state and checkpoints).  The MFMA products
+ * take their operands in bf16 whatever act_dtype and state_dtype are: q, k, v
+ * (fp32 activations are rounded once on load), the chunk's decay-weighted
+ * keys and queries, and the state where it multiplies them; accumulation,
+ * the decay factors, beta and the carried state stay fp32.
+ * The call enqueues three kernels: a small one that clears the status word
+ * and the exchange flags, the intra-chunk kernel (every chunk in parallel)
+ * and the chain kernel (the chunk-to-chunk state recurrence).  A call with
+ * more than 2^24 (chunk slot, head) pairs -- chunk slots being
  * ceil(total_tokens / chunk_size) + 2 * num_seqs -- does not fit the
- * one-dimensional grid of the first kernel and returns KDA_ERR_LAUNCH
+ * one-dimensional grid of the intra-chunk kernel and returns KDA_ERR_LAUNCH
  * without enqueuing anything.
  */
-kda_status_t kda_chunk_prefill(
+KDA_API kda_status_t kda_chunk_prefill(
     const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
     int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
     const float* g, const float* beta,
@@ -155,6 +169,23 @@ kda_status_t kda_chunk_prefill(
     float scale, int32_t chunk_size, uint32_t flags,
     void* out, int64_t out_stride_t,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostic for the prefill calls (kda_chunk_prefill, kda_chunk_prefill_at,
+ * kda_conv_chunk_prefill): waits for `stream`, then reads the status word that
+ * the last such call on `workspace` left (a call with num_seqs == 0 launches
+ * nothing and leaves it as it was).  The prefill's waves and workgroups wait
+ * for one another with bounded waits; if one ever ran out (so that call's
+ * outputs and states are not valid: the affected rows are NaN), the word is
+ * nonzero.  *device_flags (may be NULL) receives the word: bit 0 a wait ran
+ * out, bit 1 the two workgroups of a state tile ran on different XCDs.
+ * Returns KDA_OK when the word is 0, KDA_ERR_DEVICE otherwise,
+ * KDA_ERR_INVALID_ARG for a null or too small workspace (< 4 bytes) and
+ * KDA_ERR_LAUNCH if the stream or the copy fails.  Unlike every other entry
+ * point this one synchronises; it is not meant for the hot path.
+ */
+KDA_API kda_status_t kda_chunk_prefill_check(const void* workspace, size_t workspace_bytes,
+                                     uint32_t* device_flags, void* stream);
 
 /*
  * Recurrent decode: one token per row, every non-padding row has a state
@@ -171,7 +202,7 @@ kda_status_t kda_chunk_prefill(
  *   flags  KDA_FLAG_QK_L2NORM
  *   out    [batch, H, dv] of act_dtype, row stride out_stride_b
  */
-kda_status_t kda_recurrent_decode(
+KDA_API kda_status_t kda_recurrent_decode(
     const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
     int64_t q_stride_b, int64_t k_stride_b, int64_t v_stride_b,
     const float* g, const float* beta,
@@ -193,7 +224,7 @@ kda_status_t kda_recurrent_decode(
  * NULL (no affine).  dtype KDA_F32, KDA_BF16 or KDA_F16.  Math in fp32; y may
  * not alias x or gate.
  */
-kda_status_t kda_gated_rmsnorm(
+KDA_API kda_status_t kda_gated_rmsnorm(
     const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
     const void* weight, void* y, int64_t y_stride_t, kda_dtype_t dtype,
     int64_t tokens, int32_t heads, int32_t dim, float eps, void* stream);
@@ -218,7 +249,7 @@ kda_status_t kda_gated_rmsnorm(
  * output may alias an input.  kda_gated_rmsnorm is this call with no
  * residual, no bias and the SiLU gate.
  */
-kda_status_t kda_gated_rmsnorm_ex(
+KDA_API kda_status_t kda_gated_rmsnorm_ex(
     const void* x, int64_t x_stride_t, const void* gate, int64_t gate_stride_t,
     const void* residual, int64_t residual_stride_t, const void* weight, const void* bias,
     void* y, int64_t y_stride_t, void* residual_out, int64_t residual_out_stride_t,
@@ -247,7 +278,7 @@ kda_status_t kda_gated_rmsnorm_ex(
  *            not alias x.
  * Supported: width in [2, 8], channels a multiple of 8, dtype bf16 or fp32.
  */
-kda_status_t kda_causal_conv1d(
+KDA_API kda_status_t kda_causal_conv1d(
     const void* x, int64_t x_stride_t, const void* weight, const void* bias,
     void* conv_state_pool, int64_t num_slots,
     const int32_t* cu_seqlens, const int32_t* state_indices,
@@ -271,7 +302,7 @@ kda_status_t kda_causal_conv1d(
  * rows laid out sequence by sequence.  Everything else is kda_chunk_prefill
  * (same workspace query); with all positions 0 the results are identical.
  */
-kda_status_t kda_chunk_prefill_at(
+KDA_API kda_status_t kda_chunk_prefill_at(
     const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
     int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
     const float* g, const float* beta,
@@ -304,7 +335,7 @@ kda_status_t kda_chunk_prefill_at(
  * q, k).  The result equals, bit for bit, kda_causal_conv1d into a buffer y
  * followed by kda_chunk_prefill reading q, k, v from y.
  */
-kda_status_t kda_conv_chunk_prefill(
+KDA_API kda_status_t kda_conv_chunk_prefill(
     const void* x, int64_t x_stride_t, kda_dtype_t act_dtype,
     const void* conv_weight, const void* conv_bias, int32_t conv_width, uint32_t conv_flags,
     void* conv_state_pool,
@@ -341,7 +372,7 @@ kda_status_t kda_conv_chunk_prefill(
  *   flags    KDA_FLAG_QK_L2NORM
  * Supported: dk = dv in {16, 32, 64, 128}, ntok >= 1.
  */
-kda_status_t kda_spec_decode(
+KDA_API kda_status_t kda_spec_decode(
     const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
     int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
     const float* g, const float* beta,
@@ -359,31 +390,11 @@ kda_status_t kda_spec_decode(
  * contract violation and leaves that slot unchanged.  token_states and the
  * pool must not overlap.
  */
-kda_status_t kda_spec_commit(
+KDA_API kda_status_t kda_spec_commit(
     const void* token_states, int32_t batch, int32_t ntok, int32_t num_heads,
     int32_t dk, int32_t dv, const int32_t* num_accepted,
     void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
     const int32_t* state_indices, void* stream);
-
-/*
- * Per-kernel timing of kda_chunk_prefill (a benchmarking aid; not part of the
- * operator).  The prefill is two kernels on the call's stream: the
- * intra-chunk kernel (every chunk in parallel) and the chain kernel (the
- * chunk-to-chunk state recurrence).  Between kda_prefill_timing_begin and
- * kda_prefill_timing_end, each kda_chunk_prefill call, up to max_calls of
- * them, records one HIP event on its stream before the intra-chunk kernel,
- * one between the two kernels and one after the chain kernel.
- *
- * This is the library's only host-side state and its only allocation: begin
- * creates 3 * max_calls HIP events; end waits for the recorded ones, writes the
- * summed durations in milliseconds (stage_ms[0] intra-chunk, stage_ms[1]
- * chain) and the number of timed calls, and destroys the events.  Calls beyond
- * max_calls run untimed.  Not thread-safe; at most one session at a time
- * (begin while a session is open returns KDA_ERR_INVALID_ARG).  The event
- * records add a small gap between the two kernels of a timed call.
- */
-kda_status_t kda_prefill_timing_begin(int32_t max_calls);
-kda_status_t kda_prefill_timing_end(float* stage_ms, int32_t* calls);
 
 #ifdef __cplusplus
 }

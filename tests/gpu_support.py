@@ -55,12 +55,26 @@ def gpu_prefill(case: wl.PrefillCase, *, pool: torch.Tensor | None = None, chunk
         ck = torch.full((rows,) + tuple(p.shape[1:]), float("nan"), dtype=p.dtype, device=DEV)
     if flags is None:
         flags = kda.KDA_FLAG_QK_L2NORM if case.l2norm_qk else 0
-    kda.chunk_prefill(q, k, v, g, beta, cu, p, slots, out, workspace=workspace,
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(1, kda.chunk_prefill_workspace_size(
+            case.num_seqs, case.total_tokens, q.shape[1], q.shape[2], v.shape[2],
+            chunk or case.chunk_size)), dtype=torch.uint8, device=DEV)
+    kda.chunk_prefill(q, k, v, g, beta, cu, p, slots, out, workspace=ws,
                       has_initial_state=hi, checkpoints=ck, ckpt_interval=case.ckpt_interval,
                       scale=case.scale, chunk_size=chunk or case.chunk_size, flags=flags,
                       stream=stream)
     torch.cuda.synchronize()
+    assert_device_ok(ws, stream)
     return out.cpu(), p.cpu(), None if ck is None else ck.cpu()
+
+
+def assert_device_ok(ws, stream=None):
+    """The prefill's status word is 0: no bounded wait ran out and every
+    workgroup ran where the grid layout places it."""
+    from gated_delta_rule_42_amd import kda
+    word = kda.chunk_prefill_check(ws, stream=stream)
+    assert word == 0, f"prefill device status {word:#x}"
 
 
 def oracle_prefill(case: wl.PrefillCase, heads=None, pool: torch.Tensor | None = None):
