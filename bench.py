@@ -45,8 +45,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "", 0, 0),
-    "chain": (_PREFILL_SRC, "", 0, 0),
+    "intra": (_PREFILL_SRC, "d58bb98ca5fcb4dabde79c7275e240b378dcee2e57cb97a66cf95bad7cf275e3",
+              86329536, 73925152),
+    "chain": (_PREFILL_SRC, "d58bb98ca5fcb4dabde79c7275e240b378dcee2e57cb97a66cf95bad7cf275e3",
+              125751054, 68160103),
     "decode": (_DECODE_SRC, "34ff4d70888795f19b3e3393ea60a9432125b3a712f0404aca95d57dc214505c",
                547988644, 539478221),
 }
@@ -62,7 +64,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "", "profiles/prefill_T4096_H16_d128_kernel_trace.md", {})
+PROFILE_SPLIT = (_PREFILL_SRC, "d58bb98ca5fcb4dabde79c7275e240b378dcee2e57cb97a66cf95bad7cf275e3",
+                 "profiles/prefill_T4096_H16_d128_kernel_trace.md",
+                 {"intra_kernel": 39.96, "chain_kernel": 43.72})
 
 
 def profile_split():
@@ -344,6 +348,10 @@ def main() -> int:
         return 2
     K, W = args.steps, args.warmup
     result = {}
+    t_start = time.perf_counter()
+
+    def progress(leg):
+        print(f"bench.py: {leg} done at {time.perf_counter() - t_start:.1f} s", file=sys.stderr, flush=True)
     if args.only in (None, "prefill"):
         case, ms, wall, spread = bench_prefill(K, W)
         T, H, d = 4096, 16, 128
@@ -365,7 +373,7 @@ def main() -> int:
             "config": {"workload": case.name, "seqs": 1, "seq_len": T, "heads": H, "d_k": d,
                        "d_v": d, "chunk": 64, "act": "bf16", "g_beta": "fp32",
                        "state": "fp32 pool[64] slot 7", "parallelism": "none (1 GPU)"},
-            "roofline": {"kernel": "whole prefill call (flag-clearing kernel, intra_kernel, "
+            "roofline": {"kernel": "whole prefill call (intra_kernel, "
                                    "chain_kernel); the time is the call's",
                          "bound": bound,
                          "achieved": gbs if bound == "hbm" else tflops,
@@ -381,6 +389,7 @@ def main() -> int:
                          "kernel_split": profile_split()},
             "call_us_percentiles": spread,
         })
+        progress("prefill")
     if args.only in (None, "decode"):
         dcase, dms, dwall = bench_decode(K, W)
         B, H, d = 512, 16, 128
@@ -392,6 +401,7 @@ def main() -> int:
             "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": dgbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
                          "traffic": traffic_bytes("decode"), "alg_bytes": dbytes}}
+        progress("decode")
     if args.only in (None, "spec"):
         scase, sms, cms = bench_spec(K, W)
         B, ntok, H, d = scase.slots.numel(), scase.ntok, 16, 128
@@ -409,6 +419,7 @@ def main() -> int:
             "commit": {"ms_per_step": cms, "rows_accepting": n_acc,
                        "achieved": cbytes / (cms * 1e-3) / 1e9, "unit": "GB/s",
                        "alg_bytes": cbytes}}
+        progress("spec")
     if args.only in (None, "pipeline"):
         lc, pms, pwall, ums = bench_pipeline(K, W)
         result["pipeline"] = {
@@ -417,10 +428,12 @@ def main() -> int:
             "front_end": "fused conv1d + prefill (kda_conv_chunk_prefill)",
             "unfused": {"value": lc.T_call / (ums * 1e-3), "ms_per_step": ums,
                         "front_end": "kda_causal_conv1d then kda_chunk_prefill"}}
+        progress("pipeline")
     if args.only == "copy":
         result["copy"] = bench_copy(K, W)
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)
+        progress("cpu_baseline")
     if args.only is not None and "value" not in result:
         leg = result[args.only]
         result = {"metric": args.only, **leg}

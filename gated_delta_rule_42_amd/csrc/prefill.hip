@@ -470,8 +470,8 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
                   int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ g,
                   const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
                   int heads, const int32_t* __restrict__ slots, uint32_t flags,
-                  const int64_t* __restrict__ pos, uint8_t* __restrict__ ws,
-                  uint32_t* __restrict__ status, ConvIn<AT> cv)
+                  const int64_t* __restrict__ pos, uint8_t* __restrict__ ws, int64_t flag_off,
+                  int64_t n_flags, uint32_t* __restrict__ status, ConvIn<AT> cv)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NKK = P::NKK_K;
@@ -519,6 +519,16 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, g4 = lane >> 4;
 
+    if (wave == 0) {
+        // The chain kernel's flags start at zero, and so does the call's
+        // status word.  Workgroup 0 is dispatched before every other one and
+        // clears the word first thing; a bounded wait elsewhere takes
+        // milliseconds to run out, so no bit raised in this call is lost.
+        if (blockIdx.x == 0) *status = 0u;
+        uint32_t* fl = reinterpret_cast<uint32_t*>(ws + flag_off);
+        const int64_t nwg = gridDim.x;
+        for (int64_t i = (int64_t)blockIdx.x * kWave + lane; i < n_flags; i += nwg * kWave) fl[i] = 0;
+    }
     int seq = 0, first = 0;
     if (!locate_chunk(cu, pos, n_seqs, BT, x, lane, seq, first)) return;
     if (slots[seq] < 0) return;              // padding sequence: nothing to precompute
@@ -1300,9 +1310,15 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
             }
         };
         // Publishes that chunks 0 .. n - 1 are in their exchange slots.
+        // The flag is written with a plain store (a workgroup-scope atomic):
+        // the vector L1 is write-through, so the store lands in this XCD's
+        // L2, which the output workgroup (same XCD, checked through the id in
+        // the flag) polls past its own L1.  An agent-scope store would be
+        // written through to memory for the other XCDs' sake, which makes
+        // every publish wait on the memory-side round trip.
         auto publish = [&](int n) {
             if (wave == 0)
-                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(flag, (xcc << 24) | (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
         auto step = [&](int lc, const Ops& o, auto refill) {
             uint8_t* const slot_x = xch + (int64_t)lc * XSLOT;
@@ -1493,14 +1509,13 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     run_steps<NB>(nch, buf, fetch, step);
 }
 
-// Clears the status word and the chain kernel's flags before a call's
-// kernels run (a kernel, not a memset, so the call can be graph-captured).
+// Clears the status word and the chain kernel's flags for a call without
+// tokens (otherwise the intra kernel does it).
 __global__ __launch_bounds__(kThreads)
-void prefill_reset_kernel(uint32_t* __restrict__ status, uint32_t* __restrict__ flags, int64_t n_flags)
+void prefill_clear_kernel(uint32_t* __restrict__ status, uint32_t* __restrict__ flags, int64_t n_flags)
 {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_flags; i += (int64_t)gridDim.x * kThreads)
-        flags[i] = 0u;
+    if (threadIdx.x == 0) *status = 0u;
+    for (int64_t i = threadIdx.x; i < n_flags; i += kThreads) flags[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -1534,13 +1549,6 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     if (pairs > INT32_MAX) return hipErrorInvalidValue;
     uint32_t* const status = static_cast<uint32_t*>(a.workspace);
     uint8_t* const ws = static_cast<uint8_t*>(a.workspace) + kHeaderBytes;
-    {
-        const unsigned blocks = (unsigned)std::min<int64_t>(64, (lay.n_flags + kThreads - 1) / kThreads + 1);
-        hipLaunchKernelGGL(prefill_reset_kernel, dim3(blocks), dim3(kThreads), 0, stream, status,
-                           reinterpret_cast<uint32_t*>(ws + lay.flag_off), lay.n_flags);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     if (a.total_tokens > 0) {
         ConvIn<AT> cv;
         cv.w = static_cast<const AT*>(a.conv_w);
@@ -1557,13 +1565,20 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               a.seq_pos, ws, status, cv);
+                               a.seq_pos, ws, lay.flag_off, lay.n_flags, status, cv);
         else
             hipLaunchKernelGGL((intra_kernel<D, BT, AT, false>), grid, dim3(kThreads), 0, stream,
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               a.seq_pos, ws, status, cv);
+                               a.seq_pos, ws, lay.flag_off, lay.n_flags, status, cv);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        // No tokens, so no intra kernel to clear the flags and the status
+        // word: a one-workgroup kernel does it.
+        hipLaunchKernelGGL(prefill_clear_kernel, dim3(1), dim3(kThreads), 0, stream, status,
+                           reinterpret_cast<uint32_t*>(ws + lay.flag_off), lay.n_flags);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -149,9 +149,10 @@ KDA_API size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_
  * (fp32 activations are rounded once on load), the chunk's decay-weighted
  * keys and queries, and the state where it multiplies them; accumulation,
  * the decay factors, beta and the carried state stay fp32.
- * The call enqueues three kernels: a small one that clears the status word
- * and the exchange flags, the intra-chunk kernel (every chunk in parallel)
- * and the chain kernel (the chunk-to-chunk state recurrence).  A call with
+ * The call enqueues two kernels: the intra-chunk kernel (every chunk in
+ * parallel; it also clears the status word and the exchange flags) and the
+ * chain kernel (the chunk-to-chunk state recurrence); a call without tokens
+ * runs a one-workgroup clearing kernel instead of the first.  A call with
  * more than 2^24 (chunk slot, head) pairs -- chunk slots being
  * ceil(total_tokens / chunk_size) + 2 * num_seqs -- does not fit the
  * one-dimensional grid of the intra-chunk kernel and returns KDA_ERR_LAUNCH
