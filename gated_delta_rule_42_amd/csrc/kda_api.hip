@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kda_internal.h"
 
 namespace {
@@ -35,6 +37,7 @@ const char* kda_status_string(kda_status_t status)
         case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KDA_ERR_LAUNCH: return "kernel launch failed";
         case KDA_ERR_DEVICE: return "the device reported a failed call";
+        case KDA_ERR_SCRATCH_LIMIT: return "the call needs more than the library's fixed scratch area";
         default: return "unknown status";
     }
 }
@@ -133,6 +136,75 @@ kda_status_t kda_chunk_prefill(
         has_initial_state, checkpoints, ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out,
         out_stride_t, workspace, workspace_bytes);
     if (st != KDA_OK || num_seqs == 0) return st;
+    return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of kda_chunk_prefill_noalloc: a fixed array in device memory that
+// every GPU the library runs on holds from module load to process end, sized
+// for one 4096-token sequence with 16 heads of d = 128 at chunk 64 (that
+// call's workspace is 130.3 MB).  Host code never passes the array's name to
+// a kernel or a copy (on the host it names a stand-in, not device memory):
+// it uses the device address that hipGetSymbolAddress returns, looked up
+// once per device with that device current and kept in g_scratch.
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`.
+hipError_t scratch_address(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_prefill_noalloc(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t, void* stream)
+{
+    // Validated against the fixed area's size with a stand-in address (the
+    // checks only look at its alignment), so a rejected call still makes no
+    // HIP call.
+    void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+    kda::PrefillArgs a;
+    const kda_status_t st = prefill_common(
+        a, q, k, v, act_dtype, q_stride_t, k_stride_t, v_stride_t, g, beta, cu_seqlens, num_seqs,
+        total_tokens, num_heads, dk, dv, state_pool, state_dtype, num_slots, state_indices,
+        has_initial_state, checkpoints, ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out,
+        out_stride_t, stand_in, kStaticScratchBytes);
+    if (st == KDA_ERR_WORKSPACE_TOO_SMALL) return KDA_ERR_SCRATCH_LIMIT;
+    if (st != KDA_OK || num_seqs == 0) return st;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
+    a.workspace = ws;
     return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -21,6 +21,7 @@ KDA_ERR_UNSUPPORTED = 2
 KDA_ERR_WORKSPACE_TOO_SMALL = 3
 KDA_ERR_LAUNCH = 4
 KDA_ERR_DEVICE = 5
+KDA_ERR_SCRATCH_LIMIT = 6
 
 KDA_F32 = 0
 KDA_BF16 = 1
@@ -59,6 +60,13 @@ def _load() -> ctypes.CDLL:
         vp, i32, i64, vp, vp,
         vp, i64, i32,
         f32, i32, u32, vp, i64, vp, sz, vp]
+    lib.kda_chunk_prefill_noalloc.restype = i32
+    lib.kda_chunk_prefill_noalloc.argtypes = [
+        vp, vp, vp, i32, i64, i64, i64, vp, vp,
+        vp, i32, i64, i32, i32, i32,
+        vp, i32, i64, vp, vp,
+        vp, i64, i32,
+        f32, i32, u32, vp, i64, vp]
     lib.kda_chunk_prefill_at.restype = i32
     lib.kda_chunk_prefill_at.argtypes = [
         vp, vp, vp, i32, i64, i64, i64, vp, vp,
@@ -164,6 +172,19 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, 
                   flags, stream)
 
 
+def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, *,
+                          has_initial_state=None, checkpoints=None, ckpt_interval: int = 0,
+                          scale: float = 1.0, chunk_size: int = 64, flags: int = 0,
+                          stream=None) -> None:
+    """kda_chunk_prefill_noalloc: chunk_prefill on the library's fixed 128 MiB
+    scratch area instead of a workspace (nothing is allocated, here or in the
+    library).  Calls that overlap on one GPU race; a call needing more scratch
+    raises (KDA_ERR_SCRATCH_LIMIT)."""
+    _prefill_call(None, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
+                  None, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
+                  flags, stream, noalloc=True)
+
+
 def chunk_prefill_at(q, k, v, g, beta, cu_seqlens, seq_start_pos, state_pool, state_indices,
                      out, *, workspace=None, has_initial_state=None, checkpoints=None,
                      ckpt_interval: int = 0, scale: float = 1.0, chunk_size: int = 64,
@@ -179,7 +200,7 @@ def chunk_prefill_at(q, k, v, g, beta, cu_seqlens, seq_start_pos, state_pool, st
 
 def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
                   workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
-                  flags, stream) -> None:
+                  flags, stream, noalloc: bool = False) -> None:
     T, H, dk = q.shape
     dv = v.shape[2]
     N = state_indices.numel()
@@ -191,8 +212,8 @@ def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state
         _contig(has_initial_state, "has_initial_state", torch.uint8)
     if not state_pool.is_contiguous():
         raise ValueError("state_pool must be contiguous")
-    need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size)
-    if workspace is None:
+    if workspace is None and not noalloc:
+        need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     cap = 0
     if checkpoints is not None:
@@ -207,8 +228,11 @@ def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state
             _ptr(state_indices), _ptr(has_initial_state),
             _ptr(checkpoints), cap, int(ckpt_interval),
             float(scale), int(chunk_size), int(flags),
-            _ptr(out), _token_stride(out, "out"),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+            _ptr(out), _token_stride(out, "out"))
+    if noalloc:
+        _check("kda_chunk_prefill_noalloc", _lib.kda_chunk_prefill_noalloc(*head, N, *tail, _stream(stream)))
+        return
+    tail += (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if seq_start_pos is None:
         _check("kda_chunk_prefill", _lib.kda_chunk_prefill(*head, N, *tail))
     else:

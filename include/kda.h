@@ -62,6 +62,7 @@ typedef int32_t kda_status_t;
 #define KDA_ERR_WORKSPACE_TOO_SMALL 3  /* workspace_bytes below the query's result     */
 #define KDA_ERR_LAUNCH 4               /* hipGetLastError() after the launch            */
 #define KDA_ERR_DEVICE 5               /* kda_chunk_prefill_check: the device reported a failure */
+#define KDA_ERR_SCRATCH_LIMIT 6        /* kda_chunk_prefill_noalloc: call exceeds the fixed scratch */
 
 /* Element types. */
 typedef int32_t kda_dtype_t;
@@ -170,6 +171,36 @@ KDA_API kda_status_t kda_chunk_prefill(
     float scale, int32_t chunk_size, uint32_t flags,
     void* out, int64_t out_stride_t,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_prefill without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, layouts, results and
+ * errors as kda_chunk_prefill, whose kernels it runs, except that the scratch
+ * is a fixed 128 MiB area of device memory inside the library: one per GPU,
+ * held from the library's load to the end of the process.  That is enough for
+ * one 4096-token sequence with 16 heads of dk = dv = 128 at chunk 64; a call
+ * whose kda_chunk_prefill_workspace_size exceeds 128 MiB (134,217,728 bytes)
+ * returns KDA_ERR_SCRATCH_LIMIT without enqueuing anything.  The call uses the
+ * area of the current device (stream must belong to it) and allocates
+ * nothing: on its first call on a device it looks up that device's copy of
+ * the area, after which it only enqueues kernels, like kda_chunk_prefill.
+ * Every call on one GPU shares that GPU's area and leaves its contents
+ * there (the kernels clear what must start at zero): two calls that overlap
+ * on one GPU -- on different streams, or from different threads without
+ * ordering -- race and give wrong results.
+ */
+KDA_API kda_status_t kda_chunk_prefill_noalloc(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t, void* stream);
 
 /*
  * Diagnostic for the prefill calls (kda_chunk_prefill, kda_chunk_prefill_at,

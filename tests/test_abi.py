@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     from gated_delta_rule_42_amd import kda
     assert kda.abi_version() == 1
-    for code in range(6):
+    for code in range(7):
         assert kda.status_string(code) and kda.status_string(code) != "unknown status"
     assert kda.status_string(99) == "unknown status"
 
@@ -120,6 +120,30 @@ def test_prefill_validation(lib):
     assert _prefill(lib, T=1 << 26, wsb=1 << 62) == K.KDA_ERR_LAUNCH
     need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
     assert _prefill(lib, wsb=need, ws=FAKE + 16) == K.KDA_ERR_INVALID_ARG   # 256-B alignment
+
+
+def _prefill_noalloc(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, act=1, qs=2048, ks=2048, vs=2048, g=FAKE, beta=FAKE,
+             cu=FAKE, n=1, T=64, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=4, idx=FAKE,
+             hi=None, ck=None, cap=0, interval=0, scale=1.0, C=64, flags=0, out=FAKE,
+             os=2048, stream=None)
+    a.update(over)
+    return lib.kda_chunk_prefill_noalloc(*a.values())
+
+
+def test_prefill_noalloc_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+    assert _prefill_noalloc(lib, n=0) == K.KDA_OK                        # nothing to do
+    assert _prefill_noalloc(lib, dk=48, dv=48) == K.KDA_ERR_UNSUPPORTED
+    assert _prefill_noalloc(lib, q=None) == K.KDA_ERR_INVALID_ARG
+    assert _prefill_noalloc(lib, qs=1000) == K.KDA_ERR_INVALID_ARG
+    # The fixed area is 128 MiB: the headline call (one 4096-token sequence,
+    # 16 heads of d = 128, chunk 64) fits, 20,000 tokens do not and are
+    # refused on the host before any HIP call.
+    assert K.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64) <= (128 << 20)
+    assert K.chunk_prefill_workspace_size(1, 20000, 16, 128, 128, 64) > (128 << 20)
+    assert _prefill_noalloc(lib, T=20000) == K.KDA_ERR_SCRATCH_LIMIT
+    assert K.status_string(K.KDA_ERR_SCRATCH_LIMIT) != "unknown status"
 
 
 def test_prefill_check_validation(lib):
