@@ -166,10 +166,10 @@ def varlen_lengths(rng, n=8, lo=256, hi=4096, cap=16384) -> list[int]:
             return [int(x) for x in lens]
 
 
-def varlen_prefill(seed: int = 3) -> PrefillCase:
+def varlen_prefill(seed: int = 3, state_dtype=BF16) -> PrefillCase:
     """8 sequences, lengths U[256,4096] with total <= 16384, H=16, d=128,
-    bf16 q/k/v, 256-slot bf16 pool with distinct random slots, checkpoints
-    every 1024 tokens."""
+    bf16 q/k/v, 256-slot bf16 pool (or fp32: the same draws, rounded to the
+    pool dtype) with distinct random slots, checkpoints every 1024 tokens."""
     rng = np.random.default_rng(seed)
     lens = varlen_lengths(rng)
     slots = rng.choice(256, len(lens), replace=False).astype(np.int32)
@@ -177,8 +177,9 @@ def varlen_prefill(seed: int = 3) -> PrefillCase:
     cu = np.zeros(len(lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     q, k, v, g, beta = _draw_tokens(rng, int(cu[-1]), H, d, d, BF16)
-    pool = _draw_pool(rng, 256, H, d, d, BF16, 0.02)
-    return PrefillCase("varlen_prefill_8seq_H16_d128_bf16state_ckpt1024", q, k, v, g, beta,
+    pool = _draw_pool(rng, 256, H, d, d, state_dtype, 0.02)
+    tag = "bf16state" if state_dtype == BF16 else "f32state"
+    return PrefillCase(f"varlen_prefill_8seq_H16_d128_{tag}_ckpt1024", q, k, v, g, beta,
                        torch.from_numpy(cu), pool, torch.from_numpy(slots), None,
                        64, 1024, 1.0)
 

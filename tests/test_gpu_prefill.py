@@ -72,9 +72,15 @@ def test_prefill_single_sequence_full_size():
 
 def test_prefill_varlen_full_size():
     """8 sequences (<=16384 tokens), bf16 256-slot pool, checkpoints every 1024;
-    the oracle checks a sample of heads (heads are independent)."""
+    every head against the oracle."""
     case = wl.varlen_prefill()
-    check_prefill(case, gpu_prefill(case), heads=[0, 7, 15], label=case.name)
+    check_prefill(case, gpu_prefill(case), label=case.name)
+
+
+def test_prefill_varlen_full_size_fp32_state():
+    """The same batch with an fp32 pool and fp32 checkpoints (tolerance 1e-2)."""
+    case = wl.varlen_prefill(state_dtype=F32)
+    check_prefill(case, gpu_prefill(case), label=case.name)
 
 
 def test_prefill_edge_cases():
@@ -92,14 +98,29 @@ def test_prefill_edge_cases():
     assert torch.count_nonzero(o) == 0 and torch.equal(bits(p), bits(case.pool))
 
 
+def _self_diff(a, b):
+    """Two GPU runs of the same recurrence that round differently: the bf16
+    outputs' difference beyond one bf16 step of the value (two outputs a step
+    apart are equally good roundings), and the fp32 states' max-abs
+    difference."""
+    oa, ob = f64(a[0]), f64(b[0])
+    e_o = float(np.max(np.abs(oa - ob) - 2.0 ** -7 * np.maximum(np.abs(oa), np.abs(ob)), initial=0.0))
+    return e_o, max_err(f64(a[1]), f64(b[1]))
+
+
+# Bounds for GPU-against-GPU comparisons: a fraction of the oracle tolerance,
+# with room over the measured spreads (printed by each test).
+SELF_O, SELF_S = 5e-3, 5e-3
+
+
 def test_prefill_chunk_size_invariance():
     """The chunked method reaches the same result at every chunk size."""
     case = _varlen(21, 128, 64, F32, interval=0, padding=False)
     outs = [gpu_prefill(case, chunk=C) for C in (16, 32, 64)]
     for o, p, _ in outs[1:]:
-        e = max(max_err(f64(o), f64(outs[0][0])), max_err(f64(p), f64(outs[0][1])))
-        say(f"  chunk-size spread {e:.2e}")
-        assert e <= TOL[F32]
+        e_o, e_s = _self_diff((o, p), outs[0])
+        say(f"  chunk-size spread: o beyond one bf16 step {e_o:.2e}, state {e_s:.2e}")
+        assert e_o <= SELF_O and e_s <= SELF_S
 
 
 def test_prefill_split_calls_carry_state():
@@ -116,9 +137,9 @@ def test_prefill_split_calls_carry_state():
                               64, 0, 1.0)
         o, pool, _ = gpu_prefill(part)
         parts.append(o)
-    e = max(max_err(f64(torch.cat(parts)), f64(o_full)), max_err(f64(pool), f64(p_full)))
-    say(f"  split vs one call {e:.2e}")
-    assert e <= TOL[F32]
+    e_o, e_s = _self_diff((torch.cat(parts), pool), (o_full, p_full))
+    say(f"  split vs one call: o beyond one bf16 step {e_o:.2e}, state {e_s:.2e}")
+    assert e_o <= SELF_O and e_s <= SELF_S
 
 
 def test_prefill_routing_is_bit_exact():
@@ -161,9 +182,9 @@ def test_decode_equals_one_token_prefill():
                          torch.arange(41, dtype=torch.int32), case.pool, case.slots, None, 16, 0,
                          case.scale)
     o_p, p_p, _ = gpu_prefill(pre)
-    e = max(max_err(f64(o_d), f64(o_p)), max_err(f64(p_d), f64(p_p)))
-    say(f"  decode vs one-token prefill {e:.2e}")
-    assert e <= TOL[F32]
+    e_o, e_s = _self_diff((o_d, p_d), (o_p, p_p))
+    say(f"  decode vs one-token prefill: o beyond one bf16 step {e_o:.2e}, state {e_s:.2e}")
+    assert e_o <= SELF_O and e_s <= SELF_S
 
 
 def test_prefill_strided_inputs():

@@ -140,13 +140,13 @@ def test_prefill_at_resumed_sequence_matches_one_call():
     assert max(e_o, e_p, e_c) <= TOL[F32]
 
 
-def test_prefill_at_full_size_sampled_heads():
+def test_prefill_at_full_size():
     """4096 tokens, H=16, d=128, resuming at position 1000 with a bf16 state
     and checkpoints every 1024 absolute tokens (at 1024, 2048, 3072, 4096);
-    heads 0, 7 and 15 against the oracle."""
+    every head against the oracle."""
     case = wl.random_prefill(840, [4096], 16, 128, 128, state_dtype=BF16, n_slots=8, slots=[7],
                              chunk_size=64, ckpt_interval=1024, scale=inv_sqrt(128),
                              state_std=0.02)
     got = gpu_prefill_at(case, [1000])
     assert ckpt_rows(case, [1000]) == [4]
-    check_at(case, [1000], got, "prefill_at full size, start 1000", heads=[0, 7, 15])
+    check_at(case, [1000], got, "prefill_at full size, start 1000")
