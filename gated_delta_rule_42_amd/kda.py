@@ -138,6 +138,34 @@ def _token_stride(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+def _shape(t, name: str, shape, dtype=None) -> None:
+    """t (if given) has exactly `shape` (None matches any extent) and, if
+    given, `dtype`.  The C ABI takes every size from q (or x), so a tensor of
+    another shape would be read or written out of bounds: refuse it here."""
+    if t is None:
+        return
+    if t.dim() != len(shape) or any(w is not None and int(n) != int(w) for n, w in zip(t.shape, shape)):
+        want = ", ".join("*" if w is None else str(int(w)) for w in shape)
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected ({want})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} is {t.dtype}, expected {dtype}")
+
+
+def _on_device(*named) -> None:
+    """Every tensor given lives on the same GPU (host memory would reach the
+    kernels as a bad device address)."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, not on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
 def _contig(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
     if t.dtype != dtype or not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous {dtype}")
@@ -201,9 +229,27 @@ def chunk_prefill_at(q, k, v, g, beta, cu_seqlens, seq_start_pos, state_pool, st
 def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
                   workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
                   flags, stream, noalloc: bool = False) -> None:
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [tokens, heads, dim]")
     T, H, dk = q.shape
     dv = v.shape[2]
     N = state_indices.numel()
+    _shape(k, "k", (T, H, dk), q.dtype)
+    _shape(v, "v", (T, H, dv), q.dtype)
+    _shape(out, "out", (T, H, dv), q.dtype)
+    _shape(g, "g", (T, H, dk))
+    _shape(beta, "beta", (T, H))
+    _shape(cu_seqlens, "cu_seqlens", (N + 1,))
+    _shape(state_indices, "state_indices", (N,))
+    _shape(has_initial_state, "has_initial_state", (N,))
+    _shape(seq_start_pos, "seq_start_pos", (N,))
+    _shape(state_pool, "state_pool", (None, H, dk, dv))
+    _shape(checkpoints, "checkpoints", (None, H, dk, dv), state_pool.dtype)
+    _shape(workspace, "workspace", (None,), torch.uint8)
+    _on_device(("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("cu_seqlens", cu_seqlens),
+               ("state_pool", state_pool), ("state_indices", state_indices), ("out", out),
+               ("workspace", workspace), ("has_initial_state", has_initial_state),
+               ("checkpoints", checkpoints), ("seq_start_pos", seq_start_pos))
     _contig(g, "g", torch.float32)
     _contig(beta, "beta", torch.float32)
     _contig(cu_seqlens, "cu_seqlens", torch.int32)
@@ -249,15 +295,34 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
     (token stride allowed, channels contiguous); conv_weight [3Hd, W];
     conv_state_pool [slots, W-1, 3Hd] (updated in place); out [T,H,d]; the
     rest as chunk_prefill."""
+    if x.dim() != 2 or out.dim() != 3 or conv_weight.dim() != 2:
+        raise ValueError("x must be [tokens, channels], out [tokens, heads, dim], conv_weight [channels, width]")
     T, C = x.shape
     H, dv = out.shape[1], out.shape[2]
     dk = dv
     if C != 3 * H * dk:
         raise ValueError("x must hold 3*H*d channels")
+    N = state_indices.numel()
+    _shape(out, "out", (T, H, dv), x.dtype)
+    _shape(conv_weight, "conv_weight", (C, None))
+    _shape(conv_bias, "conv_bias", (C,))
+    _shape(conv_state_pool, "conv_state_pool", (None, conv_weight.shape[1] - 1, C))
+    _shape(g, "g", (T, H, dk))
+    _shape(beta, "beta", (T, H))
+    _shape(cu_seqlens, "cu_seqlens", (N + 1,))
+    _shape(state_indices, "state_indices", (N,))
+    _shape(has_initial_state, "has_initial_state", (N,))
+    _shape(state_pool, "state_pool", (None, H, dk, dv))
+    _shape(checkpoints, "checkpoints", (None, H, dk, dv), state_pool.dtype)
+    _shape(workspace, "workspace", (None,), torch.uint8)
+    _on_device(("x", x), ("conv_weight", conv_weight), ("conv_bias", conv_bias),
+               ("conv_state_pool", conv_state_pool), ("g", g), ("beta", beta),
+               ("cu_seqlens", cu_seqlens), ("state_pool", state_pool),
+               ("state_indices", state_indices), ("out", out), ("workspace", workspace),
+               ("has_initial_state", has_initial_state), ("checkpoints", checkpoints))
     if x.stride(1) != 1:
         raise ValueError("x needs contiguous channels")
     W = conv_weight.shape[1]
-    N = state_indices.numel()
     _contig(conv_weight, "conv_weight", x.dtype)
     if conv_bias is not None:
         _contig(conv_bias, "conv_bias", x.dtype)
@@ -296,8 +361,19 @@ def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, out, *, scale:
                      flags: int = 0, stream=None) -> None:
     """kda_recurrent_decode.  q,k [B,H,dk]; v,out [B,H,dv] (row-strided views
     allowed); g [B,H,dk] fp32; beta [B,H] fp32; state_pool updated in place."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [rows, heads, dim]")
     B, H, dk = q.shape
     dv = v.shape[2]
+    _shape(k, "k", (B, H, dk), q.dtype)
+    _shape(v, "v", (B, H, dv), q.dtype)
+    _shape(out, "out", (B, H, dv), q.dtype)
+    _shape(g, "g", (B, H, dk))
+    _shape(beta, "beta", (B, H))
+    _shape(state_indices, "state_indices", (B,))
+    _shape(state_pool, "state_pool", (None, H, dk, dv))
+    _on_device(("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_pool", state_pool),
+               ("state_indices", state_indices), ("out", out))
     _contig(g, "g", torch.float32)
     _contig(beta, "beta", torch.float32)
     _contig(state_indices, "state_indices", torch.int32)
@@ -318,14 +394,25 @@ def spec_decode(q, k, v, g, beta, state_pool, state_indices, token_states, out, 
     """kda_spec_decode.  q,k [B*ntok,H,dk]; v,out [B*ntok,H,dv]; g [B*ntok,H,dk]
     fp32; beta [B*ntok,H] fp32; state_pool read only; token_states
     [B,ntok,H,dk,dv] with the pool's dtype (written)."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [rows, heads, dim]")
     R, H, dk = q.shape
     dv = v.shape[2]
     B = state_indices.numel()
+    _shape(state_indices, "state_indices", (B,))
     if B == 0:
         return
     if R % B:
         raise ValueError("token rows must be batch * ntok")
     ntok = R // B
+    _shape(k, "k", (R, H, dk), q.dtype)
+    _shape(v, "v", (R, H, dv), q.dtype)
+    _shape(out, "out", (R, H, dv), q.dtype)
+    _shape(g, "g", (R, H, dk))
+    _shape(beta, "beta", (R, H))
+    _shape(state_pool, "state_pool", (None, H, dk, dv))
+    _on_device(("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_pool", state_pool),
+               ("state_indices", state_indices), ("token_states", token_states), ("out", out))
     _contig(g, "g", torch.float32)
     _contig(beta, "beta", torch.float32)
     _contig(state_indices, "state_indices", torch.int32)
@@ -346,7 +433,14 @@ def spec_decode(q, k, v, g, beta, state_pool, state_indices, token_states, out, 
 
 def spec_commit(token_states, num_accepted, state_pool, state_indices, *, stream=None) -> None:
     """kda_spec_commit: pool[slot_b] = token_states[b, num_accepted[b] - 1]."""
+    if token_states.dim() != 5:
+        raise ValueError("token_states must be [B, ntok, H, dk, dv]")
     B, ntok, H, dk, dv = token_states.shape
+    _shape(num_accepted, "num_accepted", (B,))
+    _shape(state_indices, "state_indices", (B,))
+    _shape(state_pool, "state_pool", (None, H, dk, dv))
+    _on_device(("token_states", token_states), ("num_accepted", num_accepted),
+               ("state_pool", state_pool), ("state_indices", state_indices))
     _contig(num_accepted, "num_accepted", torch.int32)
     _contig(state_indices, "state_indices", torch.int32)
     if not state_pool.is_contiguous() or state_pool.dtype != token_states.dtype:
@@ -359,7 +453,13 @@ def spec_commit(token_states, num_accepted, state_pool, state_indices, *, stream
 
 def gated_rmsnorm(x, gate, y, *, weight=None, eps: float = 1e-6, stream=None) -> None:
     """kda_gated_rmsnorm on [T,H,dim] (token-strided views allowed)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [tokens, heads, dim]")
     T, H, dim = x.shape
+    _shape(gate, "gate", (T, H, dim), x.dtype)
+    _shape(y, "y", (T, H, dim), x.dtype)
+    _shape(weight, "weight", (dim,))
+    _on_device(("x", x), ("gate", gate), ("y", y), ("weight", weight))
     if weight is not None:
         _contig(weight, "weight", x.dtype)
     status = _lib.kda_gated_rmsnorm(
@@ -374,7 +474,17 @@ def gated_rmsnorm_ex(x, gate, y, *, residual=None, residual_out=None, weight=Non
     """kda_gated_rmsnorm_ex on [T,H,dim] (token-strided views allowed).
     residual / residual_out: x's dtype, or both fp32 (KDA_NORM_RESIDUAL_F32);
     activation "silu" or "sigmoid"."""
+    if x.dim() != 3:
+        raise ValueError("x must be [tokens, heads, dim]")
     T, H, dim = x.shape
+    _shape(gate, "gate", (T, H, dim), x.dtype)
+    _shape(y, "y", (T, H, dim), x.dtype)
+    _shape(residual, "residual", (T, H, dim))
+    _shape(residual_out, "residual_out", (T, H, dim))
+    _shape(weight, "weight", (dim,))
+    _shape(bias, "bias", (dim,))
+    _on_device(("x", x), ("gate", gate), ("y", y), ("residual", residual),
+               ("residual_out", residual_out), ("weight", weight), ("bias", bias))
     if activation not in ("silu", "sigmoid"):
         raise ValueError("activation must be 'silu' or 'sigmoid'")
     for t, name in ((weight, "weight"), (bias, "bias")):
@@ -399,8 +509,21 @@ def causal_conv1d(x, weight, cu_seqlens, conv_state_pool, state_indices, y, *, b
                   has_initial_state=None, silu: bool = True, stream=None) -> None:
     """kda_causal_conv1d.  x,y [T,C] (token stride allowed, channels
     contiguous); weight [C,W]; conv_state_pool [slots,W-1,C] updated in place."""
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError("x must be [tokens, channels] and weight [channels, width]")
     T, C = x.shape
     W = weight.shape[1]
+    N = state_indices.numel()
+    _shape(y, "y", (T, C), x.dtype)
+    _shape(weight, "weight", (C, W))
+    _shape(bias, "bias", (C,))
+    _shape(conv_state_pool, "conv_state_pool", (None, W - 1, C))
+    _shape(cu_seqlens, "cu_seqlens", (N + 1,))
+    _shape(state_indices, "state_indices", (N,))
+    _shape(has_initial_state, "has_initial_state", (N,))
+    _on_device(("x", x), ("weight", weight), ("bias", bias), ("cu_seqlens", cu_seqlens),
+               ("conv_state_pool", conv_state_pool), ("state_indices", state_indices),
+               ("has_initial_state", has_initial_state), ("y", y))
     if x.stride(1) != 1 or y.stride(1) != 1:
         raise ValueError("x and y need contiguous channels")
     _contig(weight, "weight", x.dtype)
