@@ -73,7 +73,7 @@ kda_status_t prefill_common(
         ckpt_capacity < 0 || ckpt_interval < 0)
         return KDA_ERR_INVALID_ARG;
     if (!dtype_ok(act_dtype) || !dtype_ok(state_dtype)) return KDA_ERR_INVALID_ARG;
-    if (flags & ~KDA_FLAG_QK_L2NORM) return KDA_ERR_INVALID_ARG;
+    if (flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_DIAG_GIVE_UP)) return KDA_ERR_INVALID_ARG;
     if (!dim_ok(dk) || dk != dv || !chunk_ok(chunk_size)) return KDA_ERR_UNSUPPORTED;
     if (ckpt_interval > 0 && ckpt_interval % chunk_size != 0) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return KDA_OK;

@@ -1154,7 +1154,7 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                   const uint8_t* __restrict__ has_init, ST* __restrict__ ckpt, int64_t ckpt_cap,
                   int interval, float scale, AT* __restrict__ out, int64_t os,
                   uint8_t* __restrict__ ws, int64_t xch_off, int64_t xch_chunks, int64_t flag_off,
-                  uint32_t* __restrict__ status)
+                  uint32_t* __restrict__ status, int max_spin)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NB = kChainBufs;
@@ -1415,7 +1415,7 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
         auto wait_chunk = [&](int c) {             // until chunk c is published
             if (broken) return;
             uint32_t f = 0;
-            for (int spin = 0; spin < kMaxSpin; ++spin) {
+            for (int spin = 0; spin < max_spin; ++spin) {
                 // Polled with device-scope atomic loads: a plain load can keep
                 // hitting the CU's own cached copy of the flag.
                 f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1587,7 +1587,8 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                        static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                        static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
                        static_cast<AT*>(a.out), a.out_stride, ws,
-                       lay.xch_off, lay.chunks, lay.flag_off, status);
+                       lay.xch_off, lay.chunks, lay.flag_off, status,
+                       (a.flags & KDA_FLAG_DIAG_GIVE_UP) ? 0 : kMaxSpin);
     return hipGetLastError();
 }
 

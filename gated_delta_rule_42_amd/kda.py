@@ -27,6 +27,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_F16 = 2
 KDA_FLAG_QK_L2NORM = 1
+KDA_FLAG_DIAG_GIVE_UP = 0x80000000
 KDA_CONV_SILU = 1
 KDA_NORM_SIGMOID = 1
 KDA_NORM_RESIDUAL_F32 = 2

@@ -72,6 +72,12 @@ typedef int32_t kda_dtype_t;
 
 /* Flags. */
 #define KDA_FLAG_QK_L2NORM 1u   /* q, k <- x / sqrt(sum x^2 + 1e-6) per (token, head) in-kernel */
+/* Prefill diagnostic, for testing the failure report only: the chain
+ * kernel's output workgroups give up their bounded waits at once, as if the
+ * producing workgroup never published.  The call still completes normally,
+ * its output rows are NaN and its status word (kda_chunk_prefill_check)
+ * reports a wait that ran out; states and checkpoints are computed as usual. */
+#define KDA_FLAG_DIAG_GIVE_UP 0x80000000u
 #define KDA_CONV_SILU 1u        /* apply SiLU after the convolution                        */
 #define KDA_NORM_SIGMOID 1u      /* gated norm: gate activation sigmoid(z), not z*sigmoid(z) */
 #define KDA_NORM_RESIDUAL_F32 2u /* gated norm: residual and residual_out are fp32            */
@@ -131,7 +137,7 @@ KDA_API size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_
  *               skipped; floor(total_tokens / ckpt_interval) rows always
  *               suffice.  ckpt_interval must be a multiple of chunk_size.
  *   scale       output scale (1.0 gives o_t = S_t^T q_t)
- *   flags       KDA_FLAG_QK_L2NORM
+ *   flags       KDA_FLAG_QK_L2NORM, KDA_FLAG_DIAG_GIVE_UP (testing only)
  *   out         [total_tokens, H, dv] of act_dtype, token stride out_stride_t;
  *               rows of padding sequences are zeroed, rows outside every
  *               sequence are left alone.

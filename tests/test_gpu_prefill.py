@@ -206,3 +206,31 @@ def test_prefill_strided_inputs():
     o_ref, p_ref, _ = gpu_prefill(case)
     assert torch.equal(bits(out.cpu()), bits(o_ref)) and torch.equal(bits(p.cpu()), bits(p_ref))
     assert torch.count_nonzero(wide[:, H * d:]) == 0
+
+
+def test_prefill_failure_report():
+    """KDA_FLAG_DIAG_GIVE_UP makes every output workgroup give up its bounded
+    wait at once, as if its producer never published: the call completes
+    normally, the real rows come out NaN, the states are computed as usual
+    (bit for bit those of a normal call) and the status word reports the
+    wait that ran out.  The next normal call on the same workspace clears the
+    word and is correct."""
+    from gated_delta_rule_42_amd import kda
+    case = wl.random_prefill(91, [100, 37, 64], 4, 64, 64, n_slots=6, chunk_size=32,
+                             state_std=0.3)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(case.num_seqs, case.total_tokens, 4, 64, 64, 32),
+                     dtype=torch.uint8, device="cuda")
+    dev = lambda t: t.to("cuda")
+    pool = dev(case.pool).clone()
+    out = torch.zeros(case.v.shape, dtype=case.v.dtype, device="cuda")
+    kda.chunk_prefill(dev(case.q), dev(case.k), dev(case.v), dev(case.g), dev(case.beta),
+                      dev(case.cu_seqlens), pool, dev(case.slots), out, workspace=ws,
+                      chunk_size=32, flags=kda.KDA_FLAG_DIAG_GIVE_UP)
+    torch.cuda.synchronize()
+    word = kda.chunk_prefill_check(ws)
+    say(f"  status after the forced give-up: {word:#x}")
+    assert word == 1, f"status {word:#x}, expected the timeout bit alone"
+    assert torch.isnan(out.float()).all(), "rows written after a given-up wait must be NaN"
+    o_n, p_n, _ = gpu_prefill(case, workspace=ws)     # asserts the word is back to 0
+    assert torch.equal(bits(pool.cpu()), bits(p_n)), "states differ from a normal call"
+    check_prefill(case, (o_n, p_n, None), label="normal call after the forced give-up")
