@@ -266,13 +266,17 @@ _DEFAULT: Oracle | None = None
 
 
 def default() -> Oracle:
-    """The oracle built from oracle/kda_oracle.c (built on first use)."""
+    """The oracle built from oracle/kda_oracle.c (built on first use).  The
+    environment variable KDA_ORACLE_LIB names another build of the same
+    source to load instead (the sanitized one, for the sanitizer test)."""
     global _DEFAULT
     if _DEFAULT is None:
-        if not os.path.exists(_build.LIBRARY) or (
-                os.path.getmtime(_build.LIBRARY) < os.path.getmtime(_build.SOURCE)):
-            _build.build()
-        _DEFAULT = Oracle(_build.LIBRARY)
+        path = os.environ.get("KDA_ORACLE_LIB")
+        if not path:
+            path = _build.LIBRARY
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SOURCE):
+                _build.build()
+        _DEFAULT = Oracle(path)
     return _DEFAULT
 
 

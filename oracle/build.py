@@ -13,9 +13,22 @@ SOURCE = os.path.join(HERE, "kda_oracle.c")
 LIBRARY = os.path.join(HERE, "libkda_oracle.so")
 
 
-def build(source: str = SOURCE, output: str = LIBRARY, quiet: bool = True) -> str:
-    """Compile `source` with gcc into `output`; returns the library path."""
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+SANITIZED = os.path.join(HERE, "libkda_oracle_san.so")
+# Host AddressSanitizer + UndefinedBehaviorSanitizer build: every report is
+# fatal.  A process that loads it must preload libasan (the interpreter itself
+# is not instrumented).
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(source: str = SOURCE, output: str | None = None, quiet: bool = True,
+          sanitize: bool = False) -> str:
+    """Compile `source` with gcc into `output` (the plain or the sanitized
+    library by default); returns the library path."""
+    if output is None:
+        output = SANITIZED if sanitize else LIBRARY
+    opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c99", "-fopenmp", "-fPIC", "-shared",
            "-Wall", "-Werror", source, "-o", output + ".tmp", "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -272,17 +272,6 @@ int kda_oracle_decode(const double* q, const double* k, const double* v,
 }
 
 /*
- * Causal depthwise conv1d with a rolling per-sequence conv state (page "Add
- * Kimi K3 KDA execution", KDA execution step 2: run the causal convolution and
- * update its cache).  Reading taken: PyTorch cross-correlation tap order, so
- * w[c, W-1] multiplies the current token; the state holds the last W-1
- * pre-activation inputs; optional SiLU after the optional bias.
- *
- *   x, y : [T, Cch]   w : [Cch, W]   bias : [Cch] or NULL
- *   conv_pool : [n_slots, W-1, Cch], row W-2 is the most recent input
- *   slots : [n_seqs]; < 0 marks padding (zero output, no state I/O)
- */
-/*
  * Speculative multi-token decode (page "[Feature][KDA] Add Kimi K3 KDA
  * execution", Metadata construction: speculative decode is a path of its own
  * next to prefill and decode; page "FlashKDA kernel upgrade supports bf16
@@ -369,6 +358,17 @@ int kda_oracle_spec_commit(const double* token_states, int64_t B, int64_t ntok, 
     return ORACLE_OK;
 }
 
+/*
+ * Causal depthwise conv1d with a rolling per-sequence conv state (page "Add
+ * Kimi K3 KDA execution", KDA execution step 2: run the causal convolution and
+ * update its cache).  Reading taken: PyTorch cross-correlation tap order, so
+ * w[c, W-1] multiplies the current token; the state holds the last W-1
+ * pre-activation inputs; optional SiLU after the optional bias.
+ *
+ *   x, y : [T, Cch]   w : [Cch, W]   bias : [Cch] or NULL
+ *   conv_pool : [n_slots, W-1, Cch], row W-2 is the most recent input
+ *   slots : [n_seqs]; < 0 marks padding (zero output, no state I/O)
+ */
 int kda_oracle_conv1d(const double* x, const double* w, const double* bias,
                       double* conv_pool, int64_t n_slots,
                       const int64_t* cu_seqlens, const int64_t* slots,
@@ -429,9 +429,15 @@ int kda_oracle_gated_rmsnorm_ex(const double* x, const double* gate, const doubl
                                 double eps, int sigmoid, double* y, double* h_out)
 {
     if (rows < 0 || dim <= 0) return ORACLE_EINVAL;
+    int status = ORACLE_OK;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         double* h = (double*)malloc((size_t)dim * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+            continue;
+        }
         const double* gr = gate + r * dim;
         for (int64_t c = 0; c < dim; ++c)
             h[c] = x[r * dim + c] + (residual ? residual[r * dim + c] : 0.0);
@@ -446,7 +452,7 @@ int kda_oracle_gated_rmsnorm_ex(const double* x, const double* gate, const doubl
         }
         free(h);
     }
-    return ORACLE_OK;
+    return status;
 }
 
 /* The plain gated RMSNorm: no residual, no bias, SiLU gate. */
