@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(_PKG, "libkda.so")
+# KDA_LIBRARY names another build of the same sources to load instead (the
+# host-sanitized one, for the sanitizer test).
+LIBRARY = os.environ.get("KDA_LIBRARY") or os.path.join(_PKG, "libkda.so")
 
 KDA_OK = 0
 KDA_ERR_INVALID_ARG = 1
