@@ -45,12 +45,12 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "d58bb98ca5fcb4dabde79c7275e240b378dcee2e57cb97a66cf95bad7cf275e3",
-              86329536, 73925152),
-    "chain": (_PREFILL_SRC, "d58bb98ca5fcb4dabde79c7275e240b378dcee2e57cb97a66cf95bad7cf275e3",
-              125751054, 68160103),
-    "decode": (_DECODE_SRC, "34ff4d70888795f19b3e3393ea60a9432125b3a712f0404aca95d57dc214505c",
-               547988644, 539478221),
+    "intra": (_PREFILL_SRC, "0161bd7bba48e95d3c7f4f6a1da1ed023b5797cc9663f5bf92795a9136943c07",
+              86323184, 73925152),
+    "chain": (_PREFILL_SRC, "0161bd7bba48e95d3c7f4f6a1da1ed023b5797cc9663f5bf92795a9136943c07",
+              125735274, 68159539),
+    "decode": (_DECODE_SRC, "d1f466732a16d50daed458ecaa357f76aaf1a7cd8ac0d8c0bdba30a7451656b4",
+               547988774, 539453741),
 }
 
 
@@ -64,9 +64,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "d58bb98ca5fcb4dabde79c7275e240b378dcee2e57cb97a66cf95bad7cf275e3",
+PROFILE_SPLIT = (_PREFILL_SRC, "0161bd7bba48e95d3c7f4f6a1da1ed023b5797cc9663f5bf92795a9136943c07",
                  "profiles/prefill_T4096_H16_d128_kernel_trace.md",
-                 {"intra_kernel": 39.96, "chain_kernel": 43.72})
+                 {"intra_kernel": 39.86, "chain_kernel": 43.80})
 
 
 def profile_split():
