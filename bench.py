@@ -45,10 +45,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "0161bd7bba48e95d3c7f4f6a1da1ed023b5797cc9663f5bf92795a9136943c07",
-              86323184, 73925152),
-    "chain": (_PREFILL_SRC, "0161bd7bba48e95d3c7f4f6a1da1ed023b5797cc9663f5bf92795a9136943c07",
-              125735274, 68159539),
+    "intra": (_PREFILL_SRC, "2ca4a6ccc9af3cfab0de0167c8339b092a322480336ec3ff3c2b12292e162912",
+              86324723, 73925152),
+    "chain": (_PREFILL_SRC, "2ca4a6ccc9af3cfab0de0167c8339b092a322480336ec3ff3c2b12292e162912",
+              125894399, 68161277),
     "decode": (_DECODE_SRC, "d1f466732a16d50daed458ecaa357f76aaf1a7cd8ac0d8c0bdba30a7451656b4",
                547988774, 539453741),
 }
@@ -64,9 +64,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "0161bd7bba48e95d3c7f4f6a1da1ed023b5797cc9663f5bf92795a9136943c07",
+PROFILE_SPLIT = (_PREFILL_SRC, "2ca4a6ccc9af3cfab0de0167c8339b092a322480336ec3ff3c2b12292e162912",
                  "profiles/prefill_T4096_H16_d128_kernel_trace.md",
-                 {"intra_kernel": 39.86, "chain_kernel": 43.80})
+                 {"intra_kernel": 39.46, "chain_kernel": 37.87})
 
 
 def profile_split():
