@@ -14,8 +14,9 @@
 // HBM-bound (reads x, residual and gate once, writes y and residual_out
 // once).  LPR lanes share one row: each lane owns dim/LPR elements in
 // 8-element vectors, the sum of squares is reduced across the LPR lanes with
-// shuffles in a fixed order, so results are deterministic.  x (and the
-// residual) are read a second time after the reduction, from the cache.
+// shuffles in a fixed order, so results are deterministic.  When a lane
+// owns one vector, everything is loaded once before the reduction; otherwise
+// x (and the residual) are read a second time after it, from the cache.
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -103,6 +104,36 @@ void gated_rmsnorm_kernel(const T* __restrict__ x, int64_t xs, const T* __restri
             for (int i = 0; i < 8; ++i) hv[i] += rv[i];
         }
     };
+
+    if (dim == LPR * 8) {
+        // One 8-element vector per lane (dim 128 with 16 lanes per row, and
+        // every dim whose vector count is a power of two up to 64): the gate,
+        // weight and bias loads go out with x, before the reduction, and x is
+        // not read twice.  The arithmetic is that of the loop below.
+        const int c = lane_in_row * 8;
+        float hv[8], gv[8], wv[8], bv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { hv[i] = 0.0f; gv[i] = 0.0f; wv[i] = 1.0f; bv[i] = 0.0f; }
+        float ss = 0.0f;
+        if (live) {
+            row_vec(c, hv);
+            load8(gr + c, gv);
+            if (w) load8(w + c, wv);
+            if (bb) load8(bb + c, bv);
+            if (ror) store8(ror + c, hv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(hv[i], hv[i], ss);
+        }
+#pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, LPR);
+        if (!live) return;
+        const float inv = rms_inv(ss, dim, eps);
+        float out[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = gated_norm_out(hv[i], inv, wv[i], bv[i], gv[i], sig);
+        store8(yr + c, out);
+        return;
+    }
 
     // Sum of squares of h; the prenorm output is written here.
     float ss = 0.0f;
