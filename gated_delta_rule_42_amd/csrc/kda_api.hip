@@ -51,6 +51,15 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
     return kda::prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv, chunk_size);
 }
 
+size_t kda_chunk_prefill_norm_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                             int32_t num_heads, int32_t dk, int32_t dv,
+                                             int32_t chunk_size)
+{
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return 0;
+    if (!dim_ok(dk) || dk != dv || !chunk_ok(chunk_size)) return 0;
+    return kda::prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv, chunk_size, true);
+}
+
 namespace {
 
 // Checks and fills everything the two prefill entry points share.  q, k, v
@@ -111,6 +120,34 @@ kda_status_t prefill_common(
     a.seq_pos = nullptr;
     a.conv_w = a.conv_b = nullptr; a.conv_state = nullptr;
     a.conv_width = 0; a.conv_flags = 0;
+    a.norm_gate = nullptr; a.norm_gate_stride = 0; a.norm_weight = nullptr;
+    a.norm_eps = 0.0f; a.norm_y = nullptr; a.norm_y_stride = 0;
+    return KDA_OK;
+}
+
+// Checks the fused norm's arguments and the larger workspace it needs, and
+// fills them in (after prefill_common).
+kda_status_t norm_common(kda::PrefillArgs& a, const void* norm_gate, int64_t norm_gate_stride_t,
+                         const void* norm_weight, float norm_eps, void* norm_out,
+                         int64_t norm_out_stride_t, size_t workspace_bytes)
+{
+    if (!(norm_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
+    const int64_t hv = (int64_t)a.heads * a.dv;
+    if (a.total_tokens > 0 && (!norm_gate || !norm_out)) return KDA_ERR_INVALID_ARG;
+    if (norm_gate_stride_t < hv || norm_out_stride_t < hv) return KDA_ERR_INVALID_ARG;
+    if ((norm_gate_stride_t | norm_out_stride_t) & 7) return KDA_ERR_INVALID_ARG;
+    // out is read back through 32-bit byte offsets from a chunk's first row.
+    const int64_t esz = a.act == KDA_BF16 ? 2 : 4;
+    if ((int64_t)a.chunk * a.out_stride * esz >= ((int64_t)1 << 31)) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(norm_gate) || !aligned16(norm_weight) || !aligned16(norm_out))
+        return KDA_ERR_INVALID_ARG;
+    const size_t need = kda::prefill_workspace_bytes(a.num_seqs, a.total_tokens, a.heads, a.dk,
+                                                     a.dv, a.chunk, true);
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    a.norm_gate = norm_gate; a.norm_gate_stride = norm_gate_stride_t;
+    a.norm_weight = norm_weight; a.norm_eps = norm_eps;
+    a.norm_y = a.total_tokens > 0 ? norm_out : nullptr;
+    a.norm_y_stride = norm_out_stride_t;
     return KDA_OK;
 }
 
@@ -280,6 +317,78 @@ kda_status_t kda_conv_chunk_prefill(
     if (num_slots > 0 && !conv_state_pool) return KDA_ERR_INVALID_ARG;
     if (!aligned16(conv_weight) || !aligned16(conv_bias) || !aligned16(conv_state_pool))
         return KDA_ERR_INVALID_ARG;
+    a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state_pool;
+    a.conv_width = conv_width; a.conv_flags = conv_flags;
+    return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_chunk_prefill_norm(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    const void* norm_gate, int64_t norm_gate_stride_t, const void* norm_weight, float norm_eps,
+    void* norm_out, int64_t norm_out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda::PrefillArgs a;
+    kda_status_t st = prefill_common(
+        a, q, k, v, act_dtype, q_stride_t, k_stride_t, v_stride_t, g, beta, cu_seqlens, num_seqs,
+        total_tokens, num_heads, dk, dv, state_pool, state_dtype, num_slots, state_indices,
+        has_initial_state, checkpoints, ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out,
+        out_stride_t, workspace, workspace_bytes);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    st = norm_common(a, norm_gate, norm_gate_stride_t, norm_weight, norm_eps, norm_out,
+                     norm_out_stride_t, workspace_bytes);
+    if (st != KDA_OK) return st;
+    return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_conv_chunk_prefill_norm(
+    const void* x, int64_t x_stride_t, kda_dtype_t act_dtype,
+    const void* conv_weight, const void* conv_bias, int32_t conv_width, uint32_t conv_flags,
+    void* conv_state_pool,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    const void* norm_gate, int64_t norm_gate_stride_t, const void* norm_weight, float norm_eps,
+    void* norm_out, int64_t norm_out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (conv_width < 2 || conv_width > 8) return KDA_ERR_UNSUPPORTED;
+    if (conv_flags & ~KDA_CONV_SILU) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(act_dtype)) return KDA_ERR_INVALID_ARG;
+    const int64_t hd = (int64_t)num_heads * dk;
+    if (num_heads > 0 && x_stride_t < 3 * hd) return KDA_ERR_INVALID_ARG;
+    const size_t es = act_dtype == KDA_BF16 ? 2 : 4;
+    const char* xb = static_cast<const char*>(x);
+    const bool have_x = total_tokens > 0 && x;
+    kda::PrefillArgs a;
+    kda_status_t st = prefill_common(
+        a, x, have_x ? xb + hd * es : nullptr, have_x ? xb + 2 * hd * es : nullptr, act_dtype,
+        x_stride_t, x_stride_t, x_stride_t, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+        dk, dv, state_pool, state_dtype, num_slots, state_indices, has_initial_state, checkpoints,
+        ckpt_capacity, ckpt_interval, scale, chunk_size, flags, out, out_stride_t, workspace,
+        workspace_bytes);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    if (total_tokens > 0 && !conv_weight) return KDA_ERR_INVALID_ARG;
+    if (num_slots > 0 && !conv_state_pool) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(conv_weight) || !aligned16(conv_bias) || !aligned16(conv_state_pool))
+        return KDA_ERR_INVALID_ARG;
+    st = norm_common(a, norm_gate, norm_gate_stride_t, norm_weight, norm_eps, norm_out,
+                     norm_out_stride_t, workspace_bytes);
+    if (st != KDA_OK) return st;
     a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state_pool;
     a.conv_width = conv_width; a.conv_flags = conv_flags;
     return launch_status(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));

@@ -59,10 +59,18 @@ struct PrefillArgs {
     // pool is indexed like the state pool (same slots, has_init, num_slots).
     const void* conv_w; const void* conv_b; void* conv_state;
     int32_t conv_width; uint32_t conv_flags;
+    // Gated RMSNorm fused into the output (norm_y non-null): y = o *
+    // rsqrt(mean(o^2) + eps) * w * SiLU(gate) per (token, head) row of o as
+    // stored, [total_tokens, heads, dv] of act, token strides in elements.
+    const void* norm_gate; int64_t norm_gate_stride;
+    const void* norm_weight;                     // [dv] or null (= 1)
+    float norm_eps;
+    void* norm_y; int64_t norm_y_stride;
 };
-// Workspace bytes for a call; 0 if the shape is unsupported.
+// Workspace bytes for a call (with the fused norm: norm); 0 if the shape is
+// unsupported.
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t heads,
-                               int32_t dk, int32_t dv, int32_t chunk);
+                               int32_t dk, int32_t dv, int32_t chunk, bool norm = false);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 struct RmsNormArgs {

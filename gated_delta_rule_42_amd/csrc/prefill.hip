@@ -300,6 +300,7 @@ __device__ __forceinline__ bf16x8 identity_half(int half, int lane)
 
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef int v4i32 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferRsrcWord3 = 0x00020000;       // raw 32-bit buffer descriptor
 constexpr int kDeviceScope = 16;                   // cache policy: device scope (sc1)
 
@@ -1093,6 +1094,48 @@ void intra_kernel(const AT* __restrict__ q, const AT* __restrict__ k, const AT* 
     }
 }
 
+// Gated RMSNorm fused into the chain kernel's output workgroups (page
+// "[Feature][KDA] Add Kimi K3 KDA execution", What this PR does: the KDA
+// output goes through a fused normalisation-and-gating step; the result is
+// a separate buffer, o is kept).  Per (token, head) row of o as stored:
+//     y = o * rsqrt(mean(o^2) + eps) * w * SiLU(gate)
+// computed exactly as kda_gated_rmsnorm computes it (same lane layout, sum
+// chain, shuffle tree and helpers), so y is that call's result bit for bit.
+template <typename AT>
+struct NormIn {
+    const AT* gate; int64_t gs;     // [tokens, heads, D], token stride gs
+    const AT* w;                    // [D] or null (= 1)
+    AT* y; int64_t ys;              // [tokens, heads, D], token stride ys
+    float eps;
+    int64_t flag_off;               // workspace offset of the per-(pair, tile) o-stored flags
+};
+
+// Eight consecutive elements of one row, as loaded.
+template <typename AT> struct Vec8;
+template <> struct Vec8<bf16> {
+    bf16x8 v;
+    __device__ float operator[](int i) const { return static_cast<float>(v[i]); }
+};
+template <> struct Vec8<float> {
+    f32x4 a, b;
+    __device__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+__device__ __forceinline__ void load_vec8(const bf16* p, Vec8<bf16>& x) { x.v = *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void load_vec8(const float* p, Vec8<float>& x)
+{
+    x.a = *reinterpret_cast<const f32x4*>(p);
+    x.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void store_vec8(bf16* p, const float (&x)[8])
+{
+    *reinterpret_cast<bf16x8*>(p) = pack_bf16x8(x);
+}
+__device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
+{
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+
 // ---------------------------------------------------------------------------
 // chain_kernel: the state-dependent part, serial over a sequence's chunks.
 //
@@ -1137,7 +1180,10 @@ constexpr int kXchStages = 3;                      // LDS stages of S and D (out
 // workgroup publishes one every microsecond or so, so this is a safety net.
 constexpr int kMaxSpin = 1 << 20;
 
-constexpr int kSkipL1 = 1;                         // cache policy: coherent in the XCD's L2 (sc0)
+// Cache policy sc0 (workgroup scope) of the loader's copies: they read each
+// exchange slot once, after its flag, at an address this CU has not read
+// before in the launch, so no stale L1 line can answer them.
+constexpr int kSkipL1 = 1;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Marks every register of `x` as read here, so that the loads that wrote it
@@ -1145,26 +1191,69 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <typename T>
 __device__ __forceinline__ void consume(const T& x)
 {
-    constexpr int N = sizeof(T) / 16;
-    static_assert(sizeof(T) % 16 == 0, "16-byte pieces");
+    constexpr int N = sizeof(T) / 16, R = sizeof(T) % 16 / 4;
+    static_assert(sizeof(T) % 4 == 0, "4-byte pieces");
     const uint32_t* p = reinterpret_cast<const uint32_t*>(&x);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         uint32_t a = p[4 * i], b = p[4 * i + 1], c = p[4 * i + 2], d = p[4 * i + 3];
         asm volatile("" : : "v"(a), "v"(b), "v"(c), "v"(d));
     }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        uint32_t a = p[4 * N + i];
+        asm volatile("" : : "v"(a));
+    }
 }
 
-// The chunk loop of one wave with a register ring of NB chunks.  The loop
-// runs whole groups of NB steps (so every buffer is used at a fixed place in
-// the body) and the last nch % NB steps after it.  Step lc runs on the buffer
+// Loads of 4, 8 or 16 bytes at base + byte_off, coherent at device scope
+// (sc1: they miss in the CU's L1 and read the XCD's L2): for data another
+// workgroup, or this one, wrote in the same launch at an address this CU may
+// already hold in L1.  (The workgroup-scope policy, sc0, is not enough for
+// that: such a load can still return a line the L1 fetched before the
+// write.)  base must be the same for the whole wave.  Callers reinterpret the result as a float or
+// bf16 vector: indexing an integer-vector reinterpretation of it compiled,
+// with this toolchain, to one loaded element copied into every lane of the
+// vector.
+template <int BYTES>
+__device__ __forceinline__ auto load_l2(const void* base, int byte_off)
+{
+    // The base is the wave's own (the caller guarantees it); taken from the
+    // first lane so that the compiler keeps the descriptor in scalar
+    // registers instead of looping over the lanes' values.
+    // (readfirstlane returns a signed int: each half is widened through
+    // uint32_t so that a low word at or above 2^31 is not sign-extended.)
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ub), 0, 0x7fffffff,
+                                                                         kBufferRsrcWord3);
+    if constexpr (BYTES == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDeviceScope);
+    else if constexpr (BYTES == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kDeviceScope);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void load_vec8_l2(const bf16* base, int byte_off, Vec8<bf16>& x)
+{
+    x.v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(f32x4, load_l2<16>(base, byte_off)));
+}
+__device__ __forceinline__ void load_vec8_l2(const float* base, int byte_off, Vec8<float>& x)
+{
+    x.a = __builtin_bit_cast(f32x4, load_l2<16>(base, byte_off));
+    x.b = __builtin_bit_cast(f32x4, load_l2<16>(base, byte_off + 16));
+}
+
+// The chunk loop of one wave with a register ring of NB chunks, steps first
+// to nch - 1 (first a multiple of NB; the buffer of chunk lc is buf[lc % NB]).
+// The loop runs whole groups of NB steps (so every buffer is used at a fixed
+// place in the body) and the last steps after it.  Step lc runs on the buffer
 // of chunk lc and calls `refill`, which starts the loads of chunk lc + NB - 1
 // into the buffer that step lc - 1 used (its arguments go on to `fetch`, so a
 // step may start them in parts).
 template <int NB, typename Ops, typename Fetch, typename Step>
-__device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, Step step)
+__device__ __forceinline__ void run_steps(int first, int nch, Ops (&buf)[NB], Fetch fetch, Step step)
 {
-    int c0 = 0;
+    int c0 = first;
     for (; c0 + NB <= nch; c0 += NB) {
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -1180,15 +1269,168 @@ __device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, 
         }
     }
 }
+template <int NB, typename Ops, typename Fetch, typename Step>
+__device__ __forceinline__ void run_steps(int nch, Ops (&buf)[NB], Fetch fetch, Step step)
+{
+    run_steps<NB>(0, nch, buf, fetch, step);
+}
 
-template <int D, int BT, typename AT, typename ST>
+// The o-stored flags of a pair's D/16 output workgroups (with the norm
+// fused): tile t's flag holds (XCD id << 24) | the number of chunks whose o
+// that workgroup has stored.  Lane t of a wave reads tile t's, so one load
+// polls them all.
+template <int D>
+struct StoredFlags {
+    const uint32_t* f0;
+    uint32_t xcc;
+    bool mine;                                     // this lane reads a flag
+    __device__ StoredFlags(const uint32_t* f, uint32_t x, int lane) : f0(f), xcc(x), mine(lane < D / 16) {}
+    __device__ uint32_t load(int lane) const
+    {
+        return mine ? __hip_atomic_load(f0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+    __device__ bool at(uint32_t f, int n) const    // every tile has stored n chunks
+    {
+        return __all(!mine || ((f >> 24) == xcc && (int)(f & 0xffffff) >= n));
+    }
+    // Until every tile has stored n chunks; false, with the status word
+    // raised, if the bounded wait ran out.
+    __device__ bool wait(int n, int lane, int max_spin, uint32_t* status) const
+    {
+        uint32_t f = 0;
+        for (int spin = 0; spin < max_spin; ++spin) {
+            f = load(lane);
+            if (at(f, n)) return true;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const bool elsewhere = __any(mine && f != 0 && (f >> 24) != xcc);
+        raise_status(status, elsewhere ? kStatusPlacement : kStatusTimeout);
+        return false;
+    }
+};
+
+// Norm waves of an output workgroup (the norm fused into the prefill).  The
+// pair's D/16 output workgroups split each chunk's BT rows into runs of
+// RW = 16 BT / D rows in tile order, and each normalises its run with
+// kda_gated_rmsnorm's lane layout for these head dims: D/8 lanes per row, one
+// 8-element vector each, the lane's sum of squares in element order, then
+// the shuffle tree over the row's lanes.  So y is that kernel's result bit
+// for bit.
+// The waves trail the output waves by kNormLag chunks, one step per barrier
+// of the workgroup.  In step lc a wave starts the loads of o and the gate of
+// chunk lc + 2 - kNormLag and writes y of chunk lc - kNormLag from what it
+// loaded two steps earlier.  The loader has made sure, by the barrier that
+// began the step, that every tile has stored lc - 5 chunks (it checks flags
+// it loaded a step before, so it rarely waits), which covers the chunk with a
+// step to spare.  After the loop the waves wait until every tile has stored
+// all its chunks and write the rest.
+// Every step issues the same memory operations (the y store included: a lane
+// without a row of its own stores the value of a row that exists, which
+// another lane stores too), so the compiler's waits for the loads of one
+// step never hold for those of a later one.
+constexpr int kNormLag = 9;   // a multiple of kChainBufs: the write steps start on a ring boundary
+constexpr int kNormCheckLag = 4;   // the loader's check at the end of step c covers c - 4 chunks
+
+template <int D, int BT, typename AT>
+__device__ __forceinline__ void norm_rows(int nw, int lane, int tile, int nch, int off, int len, int64_t s_begin,
+                                          int h, const AT* out, int64_t os, const NormIn<AT>& nrm,
+                                          const StoredFlags<D>& flags, const int* sbroken, uint32_t* status,
+                                          int max_spin)
+{
+    constexpr int NB = kChainBufs;
+    constexpr int LPR = D / 8;                     // lanes per row
+    constexpr int RP = kWave / LPR;                // rows per wave
+    constexpr int RW = BT * 16 / D;                // rows of a chunk per tile
+    static_assert(kNormLag % NB == 0, "ring boundary");
+    // Step s loads chunk s + NB - 1 - kNormLag; the loader's check at the end
+    // of step s - 1 has every tile's chunks up to s - 2 - kNormCheckLag stored.
+    static_assert(kNormLag >= NB + 1 + kNormCheckLag, "norm lag");
+    static_assert((RW + RP - 1) / RP <= kChainWaves - 5, "norm waves");
+    if (nw * RP >= RW) return;
+    const int rl = min(nw * RP + lane / LPR, RW - 1);   // row in this tile's run
+    const int c8 = (lane % LPR) * 8;               // first column of this lane's vector
+    const int rrow = tile * RW + rl;               // row of the chunk
+    bool broken = false;
+    float wv[8];
+    if (nrm.w) {
+        Vec8<AT> t;
+        load_vec8(nrm.w + c8, t);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = t[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
+    }
+    struct Rows {
+        Vec8<AT> o, g;
+    };
+    // This lane's row of chunk c, clamped into the chunk (a run past a short
+    // last chunk reads, and later writes, the chunk's last row).
+    auto row_of = [&](int c, int64_t& t0) {
+        const int cb = chunk_begin(c, BT, off);
+        t0 = s_begin + cb;
+        return min(rrow, chunk_end(c, len, BT, off) - cb - 1);
+    };
+    auto load_rows = [&](int c, Rows& e) {
+        int64_t t0;
+        const int rr = row_of(c, t0);
+        load_vec8_l2(out + t0 * os + (int64_t)h * D, (int)(((int64_t)rr * os + c8) * (int64_t)sizeof(AT)), e.o);
+        load_vec8(nrm.gate + (t0 + rr) * nrm.gs + (int64_t)h * D + c8, e.g);
+    };
+    auto write_rows = [&](int c, const Rows& e) {
+        float hv[8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = e.o[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(hv[i], hv[i], ss);
+#pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, LPR);
+        const float inv = rms_inv(ss, D, nrm.eps);
+        const float bad = broken || *sbroken ? __builtin_nanf("") : 1.0f;
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = bad * gated_norm_out(hv[i], inv, wv[i], 0.0f, e.g[i], false);
+        int64_t t0;
+        const int rr = row_of(c, t0);
+        store_vec8(nrm.y + (t0 + rr) * nrm.ys + (int64_t)h * D + c8, y);
+    };
+    // Loads of chunk lc - kNormLag (of chunk 0 before the first, unused).
+    auto fetch = [&](int lc, Rows& e) { load_rows(max(lc - kNormLag, 0), e); };
+    Rows buf[NB];
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
+    lds_barrier();                                 // the output waves' first barrier
+    const int lead = min(nch, kNormLag);
+    run_steps<NB>(0, lead, buf, fetch, [&](int lc, const Rows&, auto refill) {
+        refill();
+        lds_barrier();                             // end of step lc
+    });
+    run_steps<NB>(kNormLag, nch, buf, fetch, [&](int lc, const Rows& e, auto refill) {
+        refill();
+        write_rows(lc - kNormLag, e);
+        lds_barrier();                             // end of step lc
+    });
+    lds_barrier();                                 // the output waves' last barrier
+    // The last kNormLag chunks (fewer in a short sequence), loaded together.
+    broken = !flags.wait(nch, lane, max_spin, status);
+    const int j0 = nch - lead;
+    Rows rest[kNormLag];
+#pragma unroll
+    for (int i = 0; i < kNormLag; ++i) load_rows(min(j0 + i, nch - 1), rest[i]);
+#pragma unroll
+    for (int i = 0; i < kNormLag; ++i)
+        if (j0 + i < nch) write_rows(j0 + i, rest[i]);
+}
+
+template <int D, int BT, typename AT, typename ST, bool NORM>
 __global__ __launch_bounds__(kChainThreads)
 void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ pos, int n_seqs, int heads,
                   ST* __restrict__ pool, int64_t num_slots, const int32_t* __restrict__ slots,
                   const uint8_t* __restrict__ has_init, ST* __restrict__ ckpt, int64_t ckpt_cap,
                   int interval, float scale, AT* __restrict__ out, int64_t os,
                   uint8_t* __restrict__ ws, int64_t xch_off, int64_t xch_chunks, int64_t flag_off,
-                  uint32_t* __restrict__ status, int max_spin)
+                  uint32_t* __restrict__ status, int max_spin, NormIn<AT> nrm)
 {
     using P = Shape<D, BT>;
     constexpr int DKP = P::DKP, BTP = P::BTP, NS = P::NS, NB = kChainBufs;
@@ -1203,12 +1445,30 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // state: bf16 D^T
     __shared__ __attribute__((aligned(1024))) uint8_t sX[kXchStages][XSLOT];   // output: S, D
 
-    // blockIdx.x enumerates (sequence, head) pairs, padded to a multiple of 8,
-    // blockIdx.y the column tile and blockIdx.z the role.
-    const int pair = blockIdx.x;
+    // Without the norm, blockIdx.x enumerates (sequence, head) pairs, padded
+    // to a multiple of 8, blockIdx.y the column tile and blockIdx.z the role.
+    // With it, the grid is one-dimensional: the state plane, then the output
+    // plane, each in blocks of 8 pairs x D/16 tiles with the pair fastest.
+    // Either way a pair's workgroups are 8 * k ids apart (one XCD), and with
+    // the norm the output workgroups of a pair, which wait for one another,
+    // sit in one block of 8 D/16 consecutive ids: blocks are dispatched in
+    // order, so the earliest unfinished block always gets the next free
+    // slots and its members are resident together.
+    int pair, tile;
+    bool state_role;
+    if constexpr (NORM) {
+        const int plane = (int)(gridDim.x / 2u), id = (int)(blockIdx.x % (unsigned)plane);
+        state_role = blockIdx.x < (unsigned)plane;
+        const int r = id % (8 * (D / 16));
+        pair = id / (8 * (D / 16)) * 8 + r % 8;
+        tile = r / 8;
+    } else {
+        pair = blockIdx.x;
+        tile = blockIdx.y;
+        state_role = blockIdx.z == 0;
+    }
     if (pair >= n_seqs * heads) return;
-    const int seq = pair / heads, h = pair % heads, tile = blockIdx.y, n0 = tile * 16;
-    const bool state_role = blockIdx.z == 0;
+    const int seq = pair / heads, h = pair % heads, n0 = tile * 16;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     __builtin_assume(wave >= 0 && wave < kChainWaves);
@@ -1221,8 +1481,17 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     const int slot = slots[seq];
     if (slot < 0) {                                // graph padding: zero output rows
         if (!state_role)
-            for (int idx = tid; idx < len * 16; idx += kChainThreads)
-                out[(s_begin + idx / 16) * os + (int64_t)h * D + n0 + idx % 16] = from_f32<AT>(0.0f);
+            for (int idx = tid; idx < len * 16; idx += kChainThreads) {
+                const int64_t at = (s_begin + idx / 16);
+                const int c = n0 + idx % 16;
+                out[at * os + (int64_t)h * D + c] = from_f32<AT>(0.0f);
+                if constexpr (NORM) {              // the norm of a zero row
+                    const float g = to_f32(nrm.gate[at * nrm.gs + (int64_t)h * D + c]);
+                    const float w = nrm.w ? to_f32(nrm.w[c]) : 1.0f;
+                    nrm.y[at * nrm.ys + (int64_t)h * D + c] =
+                        from_f32<AT>(gated_norm_out(0.0f, rms_inv(0.0f, D, nrm.eps), w, 0.0f, g, false));
+                }
+            }
         return;
     }
     if (len == 0 || slot >= num_slots) return;
@@ -1449,8 +1718,20 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     }
 
     // ---------------- output workgroup ----------------
-    if (wave > 4) return;                          // waves 5-7 have no work here
-    __shared__ int sBroken;                        // the flag never came: write NaN
+    // With the norm fused the pair's output workgroups also publish, per
+    // tile, how many chunks of o are stored (in L2, two steps late), and each
+    // normalises its share of every chunk's rows once all tiles have stored
+    // them: waves 5 and on (see norm_rows below).  Other waves past the loader
+    // have no work.
+    uint32_t* const nflag0 = NORM ? reinterpret_cast<uint32_t*>(ws + nrm.flag_off) + ((int64_t)seq * heads + h) * (D / 16)
+                                  : nullptr;
+    const StoredFlags<D> stored(nflag0, xcc, lane);
+    __shared__ int sBroken;                        // a flag never came: write NaN
+    if (wave > 4) {
+        if constexpr (NORM) norm_rows<D, BT, AT>(wave - 5, lane, tile, nch, off, len, s_begin, h, out, os, nrm,
+                                                 stored, &sBroken, status, max_spin);
+        return;
+    }
     if (wave == 4) {
         // Loader: chunk c's S and D land in stage c % kXchStages before the
         // barrier that ends step c - 1 (the prologue's barrier for c = 0).
@@ -1479,6 +1760,9 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                                                  kSkipL1);
         };
         constexpr int OPS = XSLOT / (kWave * 16);
+        // With the norm fused: the o-stored flags, loaded at the end of a
+        // step and checked at the end of the next.
+        uint32_t fnext = 0;
         wait_chunk(0); copy(0);
         wait_chunk(min(1, nch - 1)); copy(1);
         wait_vmcnt<OPS>();                         // chunk 0 landed
@@ -1490,6 +1774,13 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
             wait_chunk(min(c + 2, nch - 1));
             copy(c + 2);
             wait_vmcnt<OPS>();                     // chunk c + 1 landed
+            if constexpr (NORM) {
+                // Every tile has stored c - kNormCheckLag chunks before this
+                // step ends (the norm waves' loads of the next step need it).
+                const int n = c - kNormCheckLag;
+                if (n > 0 && !broken && !stored.at(fnext, n)) broken = !stored.wait(n, lane, max_spin, status);
+                fnext = stored.load(lane);
+            }
             if (lane == 0 && broken) sBroken = 1;
             lds_barrier();                         // end of step c
         }
@@ -1517,6 +1808,19 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
         for (int kk = 0; kk < P::NKK_T; ++kk)
             o.a[kk] = *reinterpret_cast<const bf16x8*>(rec + P::OFF_A + aq_frag(r, 32 * min(kk, kmax) + 8 * g4));
     };
+    // Loads per step of an output wave (all unconditional).
+    constexpr int LOADS_O = P::NKK_K + P::NKK_T;
+    // With the norm fused, this tile's o-stored count goes out at the end of
+    // each step: o of step lc - 2 is in L2 once at most two steps' loads
+    // remain outstanding (its store is older than both).  Like the chain's
+    // own flag, a workgroup-scope store that lands in the XCD's L2, where the
+    // pair's other workgroups read it: an agent-scope store would be written
+    // through to memory and hold up this wave's later waits.
+    auto publish_o = [&](int n) {
+        if (wave == 0 && lane == 0)
+            __hip_atomic_store(nflag0 + tile, (xcc << 24) | (uint32_t)n, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
     auto step = [&](int lc, const Ops& o, auto refill) {
         refill();
         if (active) {
@@ -1543,13 +1847,21 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
                 store4(out + (tc + r) * os + (int64_t)h * D + n0 + 4 * g4, o4);
             }
         }
+        if constexpr (NORM) wait_vmcnt<2 * LOADS_O>();
         lds_barrier();                             // end of step lc
+        if constexpr (NORM)
+            if (lc >= 1) publish_o(lc - 1);
     };
     Ops buf[NB];
 #pragma unroll
     for (int b = 0; b < NB - 1; ++b) fetch(b, buf[b]);
     lds_barrier();                                 // chunk 0 of S and D in LDS
     run_steps<NB>(nch, buf, fetch, step);
+    if constexpr (NORM) {
+        wait_vmcnt<0>();
+        lds_barrier();                             // every output wave's stores done
+        publish_o(nch);
+    }
 }
 
 // Clears the status word and the chain kernel's flags for a call without
@@ -1566,10 +1878,12 @@ void prefill_clear_kernel(uint32_t* __restrict__ status, uint32_t* __restrict__ 
 // (per head and column tile, one per chunk slot), then one flag per
 // (sequence, head, tile).
 struct WorkspaceLayout {
-    int64_t chunks, xch_off, flag_off, n_flags, bytes;
+    int64_t chunks, xch_off, flag_off, n_flags, nflag_off, bytes;
 };
+// With the norm fused the flags are followed by as many o-stored flags (so
+// the intra kernel clears both in one sweep).
 template <int D, int BT>
-WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t total_tokens, int32_t heads)
+WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t total_tokens, int32_t heads, bool norm = false)
 {
     using P = Shape<D, BT>;
     WorkspaceLayout l;
@@ -1578,15 +1892,18 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t total_tokens, int32_t
     l.xch_off = l.chunks * heads * P::REC_BYTES;
     l.flag_off = l.xch_off + (int64_t)heads * (D / 16) * l.chunks * xslot;
     l.n_flags = (int64_t)num_seqs * heads * (D / 16);
-    l.bytes = kHeaderBytes + l.flag_off + (l.n_flags * 4 + 255) / 256 * 256;
+    l.nflag_off = l.flag_off + l.n_flags * 4;
+    l.bytes = kHeaderBytes + l.flag_off + ((norm ? 2 : 1) * l.n_flags * 4 + 255) / 256 * 256;
     return l;
 }
 
 template <int D, int BT, typename AT, typename ST>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 {
-    const WorkspaceLayout lay = workspace_layout<D, BT>(a.num_seqs, a.total_tokens, a.heads);
+    const bool norm = a.norm_y != nullptr;
+    const WorkspaceLayout lay = workspace_layout<D, BT>(a.num_seqs, a.total_tokens, a.heads, norm);
     const int64_t chunks = lay.chunks;
+    const int64_t n_clear = norm ? 2 * lay.n_flags : lay.n_flags;   // chain (and norm) flags
     if (chunks * a.heads * kThreads > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 1-D intra grid
     const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;
     if (pairs > INT32_MAX) return hipErrorInvalidValue;
@@ -1608,30 +1925,49 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               a.seq_pos, ws, lay.flag_off, lay.n_flags, status, cv);
+                               a.seq_pos, ws, lay.flag_off, n_clear, status, cv);
         else
             hipLaunchKernelGGL((intra_kernel<D, BT, AT, false>), grid, dim3(kThreads), 0, stream,
                                static_cast<const AT*>(a.q), static_cast<const AT*>(a.k),
                                static_cast<const AT*>(a.v), a.q_stride, a.k_stride, a.v_stride, a.g,
                                a.beta, a.cu_seqlens, a.num_seqs, a.heads, a.slots, a.flags,
-                               a.seq_pos, ws, lay.flag_off, lay.n_flags, status, cv);
+                               a.seq_pos, ws, lay.flag_off, n_clear, status, cv);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
         // No tokens, so no intra kernel to clear the flags and the status
         // word: a one-workgroup kernel does it.
         hipLaunchKernelGGL(prefill_clear_kernel, dim3(1), dim3(kThreads), 0, stream, status,
-                           reinterpret_cast<uint32_t*>(ws + lay.flag_off), lay.n_flags);
+                           reinterpret_cast<uint32_t*>(ws + lay.flag_off), n_clear);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST>), dim3((unsigned)pairs, (unsigned)(D / 16), 2u),
-                       dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
-                       static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
-                       static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
-                       static_cast<AT*>(a.out), a.out_stride, ws,
-                       lay.xch_off, lay.chunks, lay.flag_off, status,
-                       (a.flags & KDA_FLAG_DIAG_GIVE_UP) ? 0 : kMaxSpin);
+    NormIn<AT> nrm;
+    nrm.gate = static_cast<const AT*>(a.norm_gate);
+    nrm.gs = a.norm_gate_stride;
+    nrm.w = static_cast<const AT*>(a.norm_weight);
+    nrm.y = static_cast<AT*>(a.norm_y);
+    nrm.ys = a.norm_y_stride;
+    nrm.eps = a.norm_eps;
+    nrm.flag_off = lay.nflag_off;
+    const int spin = (a.flags & KDA_FLAG_DIAG_GIVE_UP) ? 0 : kMaxSpin;
+    if (norm) {
+        const int64_t plane = pairs * (D / 16);
+        if (2 * plane > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, true>), dim3((unsigned)(2 * plane)),
+                           dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
+                           static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
+                           static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
+                           static_cast<AT*>(a.out), a.out_stride, ws,
+                           lay.xch_off, lay.chunks, lay.flag_off, status, spin, nrm);
+    } else {
+        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, false>), dim3((unsigned)pairs, (unsigned)(D / 16), 2u),
+                           dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
+                           static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
+                           static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
+                           static_cast<AT*>(a.out), a.out_stride, ws,
+                           lay.xch_off, lay.chunks, lay.flag_off, status, spin, nrm);
+    }
     return hipGetLastError();
 }
 
@@ -1659,15 +1995,15 @@ hipError_t launch_chunk(const PrefillArgs& a, hipStream_t stream)
 }  // namespace
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t heads, int32_t dk,
-                               int32_t dv, int32_t chunk)
+                               int32_t dv, int32_t chunk, bool norm)
 {
     if (dk != dv) return 0;
     auto by_chunk = [&](auto dtag) -> int64_t {
         constexpr int D = decltype(dtag)::value;
         switch (chunk) {
-            case 16: return workspace_layout<D, 16>(num_seqs, total_tokens, heads).bytes;
-            case 32: return workspace_layout<D, 32>(num_seqs, total_tokens, heads).bytes;
-            case 64: return workspace_layout<D, 64>(num_seqs, total_tokens, heads).bytes;
+            case 16: return workspace_layout<D, 16>(num_seqs, total_tokens, heads, norm).bytes;
+            case 32: return workspace_layout<D, 32>(num_seqs, total_tokens, heads, norm).bytes;
+            case 64: return workspace_layout<D, 64>(num_seqs, total_tokens, heads, norm).bytes;
             default: return 0;
         }
     };

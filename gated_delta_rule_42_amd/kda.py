@@ -84,6 +84,26 @@ def _load() -> ctypes.CDLL:
         vp, i32, i64, vp, vp,
         vp, i64, i32,
         f32, i32, u32, vp, i64, vp, sz, vp]
+    lib.kda_chunk_prefill_norm_workspace_size.restype = sz
+    lib.kda_chunk_prefill_norm_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.kda_chunk_prefill_norm.restype = i32
+    lib.kda_chunk_prefill_norm.argtypes = [
+        vp, vp, vp, i32, i64, i64, i64, vp, vp,
+        vp, i32, i64, i32, i32, i32,
+        vp, i32, i64, vp, vp,
+        vp, i64, i32,
+        f32, i32, u32, vp, i64,
+        vp, i64, vp, f32, vp, i64,
+        vp, sz, vp]
+    lib.kda_conv_chunk_prefill_norm.restype = i32
+    lib.kda_conv_chunk_prefill_norm.argtypes = [
+        vp, i64, i32, vp, vp, i32, u32, vp, vp, vp,
+        vp, i32, i64, i32, i32, i32,
+        vp, i32, i64, vp, vp,
+        vp, i64, i32,
+        f32, i32, u32, vp, i64,
+        vp, i64, vp, f32, vp, i64,
+        vp, sz, vp]
     lib.kda_recurrent_decode.restype = i32
     lib.kda_recurrent_decode.argtypes = [
         vp, vp, vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, i32,
@@ -183,24 +203,48 @@ def status_string(status: int) -> str:
 
 
 def chunk_prefill_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int,
-                                 dv: int, chunk_size: int = 64) -> int:
-    return int(_lib.kda_chunk_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv,
-                                                     chunk_size))
+                                 dv: int, chunk_size: int = 64, norm: bool = False) -> int:
+    """kda_chunk_prefill_workspace_size, or with `norm` the size the calls
+    with the fused gated norm need (kda_chunk_prefill_norm_workspace_size)."""
+    fn = _lib.kda_chunk_prefill_norm_workspace_size if norm else _lib.kda_chunk_prefill_workspace_size
+    return int(fn(num_seqs, total_tokens, num_heads, dk, dv, chunk_size))
+
+
+def _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, dtype):
+    """Checks the fused norm's tensors; None when the norm is not asked for."""
+    if norm_gate is None and norm_out is None:
+        if norm_weight is not None:
+            raise ValueError("norm_weight needs norm_gate and norm_out")
+        return None
+    if norm_gate is None or norm_out is None:
+        raise ValueError("the fused norm needs both norm_gate and norm_out")
+    _shape(norm_gate, "norm_gate", (T, H, dv), dtype)
+    _shape(norm_out, "norm_out", (T, H, dv), dtype)
+    _shape(norm_weight, "norm_weight", (dv,))
+    _on_device(("norm_gate", norm_gate), ("norm_out", norm_out), ("norm_weight", norm_weight))
+    if norm_weight is not None:
+        _contig(norm_weight, "norm_weight", dtype)
+    return (_ptr(norm_gate), _token_stride(norm_gate, "norm_gate"), _ptr(norm_weight))
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, *,
                   workspace=None, has_initial_state=None, checkpoints=None,
                   ckpt_interval: int = 0, scale: float = 1.0, chunk_size: int = 64,
-                  flags: int = 0, stream=None) -> None:
+                  flags: int = 0, norm_gate=None, norm_weight=None, norm_eps: float = 1e-6,
+                  norm_out=None, stream=None) -> None:
     """kda_chunk_prefill.  q,k [T,H,dk]; v,out [T,H,dv] (token-strided views
     allowed); g [T,H,dk] fp32; beta [T,H] fp32; cu_seqlens [N+1] int32;
     state_pool [slots,H,dk,dv] fp32/bf16 (updated in place); state_indices [N]
     int32; has_initial_state [N] uint8 or None; checkpoints [cap,H,dk,dv] or
     None.  `workspace` is a uint8 tensor of at least
-    chunk_prefill_workspace_size(...) bytes; None allocates one."""
+    chunk_prefill_workspace_size(...) bytes; None allocates one.  With
+    norm_gate and norm_out ([T,H,dv], q's dtype) and optionally norm_weight
+    [dv], kda_chunk_prefill_norm: the gated RMSNorm of out is written to
+    norm_out by the same call (workspace: chunk_prefill_workspace_size(...,
+    norm=True))."""
     _prefill_call(None, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
                   workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
-                  flags, stream)
+                  flags, stream, norm=(norm_gate, norm_weight, norm_eps, norm_out))
 
 
 def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out, *,
@@ -231,7 +275,7 @@ def chunk_prefill_at(q, k, v, g, beta, cu_seqlens, seq_start_pos, state_pool, st
 
 def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state_indices, out,
                   workspace, has_initial_state, checkpoints, ckpt_interval, scale, chunk_size,
-                  flags, stream, noalloc: bool = False) -> None:
+                  flags, stream, noalloc: bool = False, norm=(None, None, 1e-6, None)) -> None:
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q and v must be [tokens, heads, dim]")
     T, H, dk = q.shape
@@ -261,8 +305,10 @@ def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state
         _contig(has_initial_state, "has_initial_state", torch.uint8)
     if not state_pool.is_contiguous():
         raise ValueError("state_pool must be contiguous")
+    norm_gate, norm_weight, norm_eps, norm_out = norm
+    nrm = _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, q.dtype)
     if workspace is None and not noalloc:
-        need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size)
+        need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size, norm=nrm is not None)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     cap = 0
     if checkpoints is not None:
@@ -281,7 +327,13 @@ def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state
     if noalloc:
         _check("kda_chunk_prefill_noalloc", _lib.kda_chunk_prefill_noalloc(*head, N, *tail, _stream(stream)))
         return
-    tail += (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    ws_tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if nrm is not None:
+        _check("kda_chunk_prefill_norm",
+               _lib.kda_chunk_prefill_norm(*head, N, *tail, *nrm, float(norm_eps), _ptr(norm_out),
+                                           _token_stride(norm_out, "norm_out"), *ws_tail))
+        return
+    tail += ws_tail
     if seq_start_pos is None:
         _check("kda_chunk_prefill", _lib.kda_chunk_prefill(*head, N, *tail))
     else:
@@ -293,11 +345,13 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
                        state_indices, out, *, conv_bias=None, silu: bool = True, workspace=None,
                        has_initial_state=None, checkpoints=None, ckpt_interval: int = 0,
                        scale: float = 1.0, chunk_size: int = 64, flags: int = 0,
+                       norm_gate=None, norm_weight=None, norm_eps: float = 1e-6, norm_out=None,
                        stream=None) -> None:
     """kda_conv_chunk_prefill.  x [T, 3*H*d] packed q|k|v before the conv
     (token stride allowed, channels contiguous); conv_weight [3Hd, W];
     conv_state_pool [slots, W-1, 3Hd] (updated in place); out [T,H,d]; the
-    rest as chunk_prefill."""
+    rest as chunk_prefill, the fused norm included
+    (kda_conv_chunk_prefill_norm)."""
     if x.dim() != 2 or out.dim() != 3 or conv_weight.dim() != 2:
         raise ValueError("x must be [tokens, channels], out [tokens, heads, dim], conv_weight [channels, width]")
     T, C = x.shape
@@ -339,7 +393,8 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
         _contig(has_initial_state, "has_initial_state", torch.uint8)
     if not state_pool.is_contiguous():
         raise ValueError("state_pool must be contiguous")
-    need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size)
+    nrm = _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, x.dtype)
+    need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size, norm=nrm is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     cap = 0
@@ -347,7 +402,7 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
         if not checkpoints.is_contiguous() or checkpoints.dtype != state_pool.dtype:
             raise ValueError("checkpoints must be contiguous with the state dtype")
         cap = checkpoints.shape[0]
-    status = _lib.kda_conv_chunk_prefill(
+    args = (
         _ptr(x), x.stride(0), _dtype(x), _ptr(conv_weight), _ptr(conv_bias), W,
         KDA_CONV_SILU if silu else 0, _ptr(conv_state_pool),
         _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
@@ -355,9 +410,14 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
         _ptr(state_indices), _ptr(has_initial_state),
         _ptr(checkpoints), cap, int(ckpt_interval),
         float(scale), int(chunk_size), int(flags),
-        _ptr(out), _token_stride(out, "out"),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("kda_conv_chunk_prefill", status)
+        _ptr(out), _token_stride(out, "out"))
+    ws_tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if nrm is not None:
+        _check("kda_conv_chunk_prefill_norm",
+               _lib.kda_conv_chunk_prefill_norm(*args, *nrm, float(norm_eps), _ptr(norm_out),
+                                                _token_stride(norm_out, "norm_out"), *ws_tail))
+        return
+    _check("kda_conv_chunk_prefill", _lib.kda_conv_chunk_prefill(*args, *ws_tail))
 
 
 def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, out, *, scale: float = 1.0,

@@ -388,6 +388,73 @@ KDA_API kda_status_t kda_conv_chunk_prefill(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill with the gated RMSNorm fused into its output (page "[Feature][KDA]
+ * Add Kimi K3 KDA execution", What this PR does: the KDA output goes through
+ * a fused normalisation-and-gating step whose result is allocated
+ * separately, so the KDA output itself is kept).  Besides everything
+ * kda_chunk_prefill (or kda_conv_chunk_prefill) computes and writes, including
+ * `out`, these write
+ *   norm_out[t, h, :] = out[t, h, :] * rsqrt(mean(out[t, h, :]^2) + norm_eps)
+ *                       * norm_weight * SiLU(norm_gate[t, h, :])
+ * for every token row, out taken as stored (act_dtype); norm_out equals, bit
+ * for bit, kda_gated_rmsnorm(out, norm_gate, norm_weight, norm_eps) after the
+ * plain call.  Padding sequences (state index < 0) get the norm of their zero
+ * rows, as that call would give them.
+ *   norm_gate  [total_tokens, H, dv] of act_dtype, token stride
+ *              norm_gate_stride_t (elements, >= H*dv, a multiple of 8)
+ *   norm_weight [dv] of act_dtype or NULL (= 1);  norm_eps >= 0
+ *   norm_out   [total_tokens, H, dv] of act_dtype, token stride
+ *              norm_out_stride_t (same rules); must not overlap out
+ *   workspace  at least kda_chunk_prefill_norm_workspace_size(...) bytes (the
+ *              plain size plus a second flag per (sequence, head, 16-column
+ *              tile)), 256-byte aligned
+ * The output workgroups of a (sequence, head) tell one another through those
+ * flags which chunks of `out` are stored, and each then normalises a share of
+ * the chunk's rows; the same device-side status word reports a bounded wait
+ * that ran out (kda_chunk_prefill_check).  Returns as kda_chunk_prefill, and
+ * KDA_ERR_INVALID_ARG for a missing norm_gate / norm_out with tokens, a bad
+ * stride (including an out_stride_t with chunk_size * out_stride_t *
+ * element size at or above 2^31 bytes), a misaligned pointer or a negative
+ * (or NaN) norm_eps.
+ * Cost: the call saves a launch and the second read of `out`, but the norm's
+ * loads and stores join the prefill's serial chunk steps; at 4096 tokens x 16
+ * heads of dv = 128 it is slower than the plain call followed by
+ * kda_gated_rmsnorm.
+ */
+KDA_API size_t kda_chunk_prefill_norm_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                                     int32_t num_heads, int32_t dk, int32_t dv,
+                                                     int32_t chunk_size);
+KDA_API kda_status_t kda_chunk_prefill_norm(
+    const void* q, const void* k, const void* v, kda_dtype_t act_dtype,
+    int64_t q_stride_t, int64_t k_stride_t, int64_t v_stride_t,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    const void* norm_gate, int64_t norm_gate_stride_t, const void* norm_weight, float norm_eps,
+    void* norm_out, int64_t norm_out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream);
+KDA_API kda_status_t kda_conv_chunk_prefill_norm(
+    const void* x, int64_t x_stride_t, kda_dtype_t act_dtype,
+    const void* conv_weight, const void* conv_bias, int32_t conv_width, uint32_t conv_flags,
+    void* conv_state_pool,
+    const float* g, const float* beta,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+    int32_t num_heads, int32_t dk, int32_t dv,
+    void* state_pool, kda_dtype_t state_dtype, int64_t num_slots,
+    const int32_t* state_indices, const uint8_t* has_initial_state,
+    void* checkpoints, int64_t ckpt_capacity, int32_t ckpt_interval,
+    float scale, int32_t chunk_size, uint32_t flags,
+    void* out, int64_t out_stride_t,
+    const void* norm_gate, int64_t norm_gate_stride_t, const void* norm_weight, float norm_eps,
+    void* norm_out, int64_t norm_out_stride_t,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Speculative multi-token decode (page "[Feature][KDA] Add Kimi K3 KDA
  * execution", Metadata construction: speculative decode is a path of its own
  * next to chunk prefill and recurrent decode; page "FlashKDA kernel upgrade

@@ -36,6 +36,8 @@ def test_header_declares_the_entry_points():
                  "kda_causal_conv1d", "kda_chunk_prefill_workspace_size",
                  "kda_conv_chunk_prefill", "kda_gated_rmsnorm_ex", "kda_chunk_prefill_at",
                  "kda_spec_decode", "kda_spec_commit", "kda_chunk_prefill_check",
+                 "kda_chunk_prefill_norm", "kda_conv_chunk_prefill_norm",
+                 "kda_chunk_prefill_norm_workspace_size",
                  "kda_abi_version", "kda_status_string"):
         assert want in names
 
@@ -80,6 +82,13 @@ def test_workspace_size(lib):
     for bad in [(1, 64, 1, 48, 48, 64), (1, 64, 1, 128, 64, 64), (1, 64, 1, 128, 128, 48),
                 (-1, 64, 1, 128, 128, 64), (1, 64, 0, 128, 128, 64)]:
         assert kda.chunk_prefill_workspace_size(*bad) == 0
+        assert kda.chunk_prefill_workspace_size(*bad, norm=True) == 0
+    # With the fused norm: a second flag per (sequence, head, tile) right
+    # after the first, both in one 256-byte aligned block.
+    body = (64 + 2) * 16 * per_slot
+    n_flags = 1 * 16 * (128 // 16)
+    assert (kda.chunk_prefill_workspace_size(1, 4096, 16, 128, 128, 64, norm=True)
+            == header + body + (2 * n_flags * 4 + 255) // 256 * 256)
 
 
 FAKE = 0x10000   # aligned, never dereferenced: every call below stops in validation
@@ -284,3 +293,57 @@ def test_norm_and_conv_validation(lib):
     assert c(w=None) == K.KDA_ERR_INVALID_ARG
     assert c(xs=100) == K.KDA_ERR_INVALID_ARG
     assert c(flags=4) == K.KDA_ERR_INVALID_ARG
+
+
+def _norm_tail(over):
+    t = dict(ngate=FAKE, ngs=2048, nw=None, neps=1e-6, nout=FAKE, nos=2048)
+    t.update({k: v for k, v in over.items() if k in t})
+    return t
+
+
+def _prefill_norm(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, act=1, qs=2048, ks=2048, vs=2048, g=FAKE, beta=FAKE,
+             cu=FAKE, n=1, T=64, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=4, idx=FAKE,
+             hi=None, ck=None, cap=0, interval=0, scale=1.0, C=64, flags=0, out=FAKE,
+             os=2048)
+    a.update({k: v for k, v in over.items() if k in a})
+    w = dict(ws=FAKE, wsb=0, stream=None)
+    w.update({k: v for k, v in over.items() if k in w})
+    return lib.kda_chunk_prefill_norm(*a.values(), *_norm_tail(over).values(), *w.values())
+
+
+def _conv_prefill_norm(lib, **over):
+    a = dict(x=FAKE, xs=6144, act=1, w=FAKE, b=None, W=4, cflags=1, cpool=FAKE, g=FAKE,
+             beta=FAKE, cu=FAKE, n=1, T=64, H=16, dk=128, dv=128, pool=FAKE, sdt=0, slots=4,
+             idx=FAKE, hi=None, ck=None, cap=0, interval=0, scale=1.0, C=64, flags=1,
+             out=FAKE, os=2048)
+    a.update({k: v for k, v in over.items() if k in a})
+    w = dict(ws=FAKE, wsb=0, stream=None)
+    w.update({k: v for k, v in over.items() if k in w})
+    return lib.kda_conv_chunk_prefill_norm(*a.values(), *_norm_tail(over).values(), *w.values())
+
+
+def test_prefill_norm_validation(lib):
+    from gated_delta_rule_42_amd import kda as K
+    plain = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64)
+    need = K.chunk_prefill_workspace_size(1, 64, 16, 128, 128, 64, norm=True)
+    assert need > plain
+    for call in (_prefill_norm, _conv_prefill_norm):
+        assert call(lib, n=0) == K.KDA_OK                               # nothing to do
+        assert call(lib, dk=48, dv=48, xs=3 * 16 * 48) == K.KDA_ERR_UNSUPPORTED
+        # The plain prefill's workspace is not enough for the fused norm.
+        assert call(lib, wsb=plain) == K.KDA_ERR_WORKSPACE_TOO_SMALL
+        assert call(lib, wsb=need, ngate=None) == K.KDA_ERR_INVALID_ARG
+        assert call(lib, wsb=need, nout=None) == K.KDA_ERR_INVALID_ARG
+        assert call(lib, wsb=need, ngs=1000) == K.KDA_ERR_INVALID_ARG   # < H * dv
+        assert call(lib, wsb=need, nos=2052) == K.KDA_ERR_INVALID_ARG   # not a multiple of 8
+        assert call(lib, wsb=need, neps=-1.0) == K.KDA_ERR_INVALID_ARG
+        assert call(lib, wsb=need, neps=float("nan")) == K.KDA_ERR_INVALID_ARG
+        assert call(lib, wsb=need, nw=FAKE + 4) == K.KDA_ERR_INVALID_ARG   # misaligned
+        assert call(lib, wsb=need, nout=FAKE + 8) == K.KDA_ERR_INVALID_ARG
+        # 64 rows of out at this stride span 2^31 bytes: past the 32-bit
+        # offsets the norm reads out with (the plain prefill takes it).
+        assert call(lib, wsb=need, os=1 << 24) == K.KDA_ERR_INVALID_ARG
+    # The conv front end's own checks still apply.
+    assert _conv_prefill_norm(lib, wsb=need, W=9) == K.KDA_ERR_UNSUPPORTED
+    assert _conv_prefill_norm(lib, wsb=need, w=None) == K.KDA_ERR_INVALID_ARG

@@ -8,7 +8,15 @@ bounded wait always ends.  The GPU deals the workgroups of a launch to its 8
 XCDs round-robin by linear id x + X (y + Y z) and dispatches them in
 linear-id order.  This test checks that the chain kernel's source launches
 the grid modelled here, then enumerates that grid for every shape the tests
-and the bench launch (and more) and checks both properties."""
+and the bench launch (and more) and checks both properties.
+
+With the gated norm fused, the grid is one-dimensional (the state plane, then
+the output plane, each in blocks of 8 pairs x d/16 tiles, pair fastest) and
+the output workgroups of a pair also wait for one another.  Besides the two
+properties above, a pair's workgroups must then all share one XCD and its
+output workgroups lie in one block of 8 d/16 consecutive ids, so that the
+earliest unfinished block, whose members wait only for each other and for
+earlier workgroups, is always dispatched whole."""
 import os
 import re
 
@@ -29,11 +37,20 @@ def chain_grid(num_seqs: int, heads: int, d: int):
 def test_source_launches_the_modelled_grid():
     src = open(SRC).read()
     assert "const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;" in src
-    assert re.search(r"chain_kernel<D, BT, AT, ST>\)\s*,\s*dim3\(\(unsigned\)pairs, \(unsigned\)\(D / 16\), 2u\)",
+    assert re.search(r"chain_kernel<D, BT, AT, ST, false>\)\s*,\s*dim3\(\(unsigned\)pairs, \(unsigned\)\(D / 16\), 2u\)",
                      src), "chain_kernel launch geometry changed"
-    assert "const int pair = blockIdx.x;" in src
-    assert "tile = blockIdx.y" in src
-    assert "const bool state_role = blockIdx.z == 0;" in src
+    assert "pair = blockIdx.x;" in src
+    assert "tile = blockIdx.y;" in src
+    assert "state_role = blockIdx.z == 0;" in src
+    # The fused-norm grid.
+    assert "const int64_t plane = pairs * (D / 16);" in src
+    assert re.search(r"chain_kernel<D, BT, AT, ST, true>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)", src)
+    for line in ("const int plane = (int)(gridDim.x / 2u), id = (int)(blockIdx.x % (unsigned)plane);",
+                 "state_role = blockIdx.x < (unsigned)plane;",
+                 "const int r = id % (8 * (D / 16));",
+                 "pair = id / (8 * (D / 16)) * 8 + r % 8;",
+                 "tile = r / 8;"):
+        assert line in src, line
 
 
 SHAPES = sorted({
@@ -61,3 +78,36 @@ def test_tile_roles_share_an_xcd_and_the_producer_comes_first(n, h, d):
 def test_varlen_batch_grid_size():
     X, Y, Z = chain_grid(8, 16, 128)
     assert X * Y * Z == 2048
+
+
+def norm_grid_decode(L: int, plane: int, d: int):
+    """(pair, tile, state_role) of linear id L in the fused-norm grid, as the
+    kernel computes it."""
+    Y = d // 16
+    i = L % plane
+    r = i % (8 * Y)
+    return i // (8 * Y) * 8 + r % 8, r // 8, L < plane
+
+
+@pytest.mark.parametrize("n,h,d", SHAPES)
+def test_norm_grid_placement(n, h, d):
+    X, Y, _ = chain_grid(n, h, d)
+    plane = X * Y
+    seen = {}
+    for L in range(2 * plane):
+        pair, tile, state = norm_grid_decode(L, plane, d)
+        assert 0 <= tile < Y and 0 <= pair < X
+        seen[(pair, tile, state)] = L
+    assert len(seen) == 2 * plane                       # every (pair, tile, role) once
+    block = 8 * Y
+    for pair in range(n * h):
+        ids = [seen[(pair, t, s)] for t in range(Y) for s in (True, False)]
+        assert len({L % XCDS for L in ids}) == 1           # one XCD for the whole pair
+        for t in range(Y):
+            assert seen[(pair, t, True)] < seen[(pair, t, False)]   # producer first
+        outs = [seen[(pair, t, False)] - plane for t in range(Y)]
+        assert len({o // block for o in outs}) == 1        # one block of the output plane
+    # Output workgroups wait only on their own block and on earlier ids (the
+    # state plane), so dispatch in id order can always finish the earliest
+    # unfinished block: it needs 8 d/16 <= 64 slots.
+    assert block <= 64
