@@ -19,7 +19,8 @@ activations (each ~80 MB).  The same line carries:
     (draft tokens/s; state after every token written), and its commit;
   * pipeline: tokens/s of one 4096-token call of the long-context pipeline
     (conv1d -> prefill with q/k L2 norm, bf16 state, checkpoint -> gated RMSNorm),
-    with the conv fused into the prefill, and the unfused calls beside it;
+    with the conv fused into the prefill, the unfused calls and the call with
+    the norm fused into the prefill as well beside it;
   * roofline objects (algorithmic bytes / measured time against 8 TB/s);
   * cpu_baseline: the fp64 oracle timed on the host on the same prefill
     workload (bounded to ~10 s).
@@ -45,10 +46,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "2ca4a6ccc9af3cfab0de0167c8339b092a322480336ec3ff3c2b12292e162912",
-              86324723, 73925152),
-    "chain": (_PREFILL_SRC, "2ca4a6ccc9af3cfab0de0167c8339b092a322480336ec3ff3c2b12292e162912",
-              125894399, 68161277),
+    "intra": (_PREFILL_SRC, "3eb252ad5f1bd5022a7c5d1a226e24d1f6fb9171cac4503b2b4cb2723a277371",
+              86299151, 73925120),
+    "chain": (_PREFILL_SRC, "3eb252ad5f1bd5022a7c5d1a226e24d1f6fb9171cac4503b2b4cb2723a277371",
+              125878007, 68161946),
     "decode": (_DECODE_SRC, "d1f466732a16d50daed458ecaa357f76aaf1a7cd8ac0d8c0bdba30a7451656b4",
                547988774, 539453741),
 }
@@ -64,9 +65,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "2ca4a6ccc9af3cfab0de0167c8339b092a322480336ec3ff3c2b12292e162912",
+PROFILE_SPLIT = (_PREFILL_SRC, "3eb252ad5f1bd5022a7c5d1a226e24d1f6fb9171cac4503b2b4cb2723a277371",
                  "profiles/prefill_T4096_H16_d128_kernel_trace.md",
-                 {"intra_kernel": 39.46, "chain_kernel": 37.87})
+                 {"intra_kernel": 39.47, "chain_kernel": 38.52})
 
 
 def profile_split():
@@ -263,8 +264,8 @@ def bench_pipeline(steps: int, warmup: int):
     y = torch.empty(T, lc.channels, dtype=torch.bfloat16, device=dev)
     o = torch.empty(T, H, d, dtype=torch.bfloat16, device=dev)
     z = torch.empty_like(o)
-    ws = torch.empty(kda.chunk_prefill_workspace_size(1, T, H, d, d, 64), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(1, T, H, d, d, 64, norm=True),
+                     dtype=torch.uint8, device=dev)
     hd = H * d
 
     def unfused(i):
@@ -281,9 +282,16 @@ def bench_pipeline(steps: int, warmup: int):
                                flags=kda.KDA_FLAG_QK_L2NORM)
         kda.gated_rmsnorm(o, gate, z, weight=nw, eps=lc.eps)
 
+    def norm_fused(i):
+        kda.conv_chunk_prefill(x, w, conv_pool, g, beta, cu, pool, slot, o, workspace=ws,
+                               checkpoints=ckpt, ckpt_interval=T, chunk_size=64,
+                               flags=kda.KDA_FLAG_QK_L2NORM, norm_gate=gate, norm_weight=nw,
+                               norm_eps=lc.eps, norm_out=z)
+
     ums, _ = time_calls(unfused, steps, warmup)
+    nms, _ = time_calls(norm_fused, steps, warmup)
     ms, wall = time_calls(fused, steps, warmup)
-    return lc, ms, wall, ums
+    return lc, ms, wall, ums, nms
 
 
 def bench_copy(steps: int, warmup: int, nbytes: int = 1 << 30):
@@ -421,13 +429,15 @@ def main() -> int:
                        "alg_bytes": cbytes}}
         progress("spec")
     if args.only in (None, "pipeline"):
-        lc, pms, pwall, ums = bench_pipeline(K, W)
+        lc, pms, pwall, ums, nms = bench_pipeline(K, W)
         result["pipeline"] = {
             "value": lc.T_call / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms,
             "steps": K, "workload": lc.name + " (one 4096-token call per step)",
             "front_end": "fused conv1d + prefill (kda_conv_chunk_prefill)",
             "unfused": {"value": lc.T_call / (ums * 1e-3), "ms_per_step": ums,
-                        "front_end": "kda_causal_conv1d then kda_chunk_prefill"}}
+                        "front_end": "kda_causal_conv1d then kda_chunk_prefill"},
+            "norm_fused": {"value": lc.T_call / (nms * 1e-3), "ms_per_step": nms,
+                           "front_end": "kda_conv_chunk_prefill_norm (the norm in the prefill)"}}
         progress("pipeline")
     if args.only == "copy":
         result["copy"] = bench_copy(K, W)
