@@ -211,7 +211,9 @@ def chunk_prefill_workspace_size(num_seqs: int, total_tokens: int, num_heads: in
 
 
 def _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, dtype):
-    """Checks the fused norm's tensors; None when the norm is not asked for."""
+    """Checks the fused norm's tensors' shapes and dtypes (their device is
+    checked with the call's other tensors); None when the norm is not asked
+    for."""
     if norm_gate is None and norm_out is None:
         if norm_weight is not None:
             raise ValueError("norm_weight needs norm_gate and norm_out")
@@ -221,7 +223,15 @@ def _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, dtype):
     _shape(norm_gate, "norm_gate", (T, H, dv), dtype)
     _shape(norm_out, "norm_out", (T, H, dv), dtype)
     _shape(norm_weight, "norm_weight", (dv,))
-    _on_device(("norm_gate", norm_gate), ("norm_out", norm_out), ("norm_weight", norm_weight))
+    return norm_gate, norm_out, norm_weight
+
+
+def _norm_ptrs(nrm, dtype):
+    """(gate pointer, gate token stride, weight pointer) of checked norm
+    tensors, None for none."""
+    if nrm is None:
+        return None
+    norm_gate, _, norm_weight = nrm
     if norm_weight is not None:
         _contig(norm_weight, "norm_weight", dtype)
     return (_ptr(norm_gate), _token_stride(norm_gate, "norm_gate"), _ptr(norm_weight))
@@ -293,10 +303,13 @@ def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state
     _shape(state_pool, "state_pool", (None, H, dk, dv))
     _shape(checkpoints, "checkpoints", (None, H, dk, dv), state_pool.dtype)
     _shape(workspace, "workspace", (None,), torch.uint8)
+    norm_gate, norm_weight, norm_eps, norm_out = norm
+    nrm = _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, q.dtype)
     _on_device(("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("cu_seqlens", cu_seqlens),
                ("state_pool", state_pool), ("state_indices", state_indices), ("out", out),
                ("workspace", workspace), ("has_initial_state", has_initial_state),
-               ("checkpoints", checkpoints), ("seq_start_pos", seq_start_pos))
+               ("checkpoints", checkpoints), ("seq_start_pos", seq_start_pos),
+               ("norm_gate", norm_gate), ("norm_out", norm_out), ("norm_weight", norm_weight))
     _contig(g, "g", torch.float32)
     _contig(beta, "beta", torch.float32)
     _contig(cu_seqlens, "cu_seqlens", torch.int32)
@@ -305,8 +318,7 @@ def _prefill_call(seq_start_pos, q, k, v, g, beta, cu_seqlens, state_pool, state
         _contig(has_initial_state, "has_initial_state", torch.uint8)
     if not state_pool.is_contiguous():
         raise ValueError("state_pool must be contiguous")
-    norm_gate, norm_weight, norm_eps, norm_out = norm
-    nrm = _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, q.dtype)
+    nrm = _norm_ptrs(nrm, q.dtype)
     if workspace is None and not noalloc:
         need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size, norm=nrm is not None)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -372,11 +384,13 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
     _shape(state_pool, "state_pool", (None, H, dk, dv))
     _shape(checkpoints, "checkpoints", (None, H, dk, dv), state_pool.dtype)
     _shape(workspace, "workspace", (None,), torch.uint8)
+    nrm = _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, x.dtype)
     _on_device(("x", x), ("conv_weight", conv_weight), ("conv_bias", conv_bias),
                ("conv_state_pool", conv_state_pool), ("g", g), ("beta", beta),
                ("cu_seqlens", cu_seqlens), ("state_pool", state_pool),
                ("state_indices", state_indices), ("out", out), ("workspace", workspace),
-               ("has_initial_state", has_initial_state), ("checkpoints", checkpoints))
+               ("has_initial_state", has_initial_state), ("checkpoints", checkpoints),
+               ("norm_gate", norm_gate), ("norm_out", norm_out), ("norm_weight", norm_weight))
     if x.stride(1) != 1:
         raise ValueError("x needs contiguous channels")
     W = conv_weight.shape[1]
@@ -393,7 +407,7 @@ def conv_chunk_prefill(x, conv_weight, conv_state_pool, g, beta, cu_seqlens, sta
         _contig(has_initial_state, "has_initial_state", torch.uint8)
     if not state_pool.is_contiguous():
         raise ValueError("state_pool must be contiguous")
-    nrm = _norm_args(norm_gate, norm_weight, norm_out, T, H, dv, x.dtype)
+    nrm = _norm_ptrs(nrm, x.dtype)
     need = chunk_prefill_workspace_size(N, T, H, dk, dv, chunk_size, norm=nrm is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)

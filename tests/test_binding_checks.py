@@ -134,3 +134,27 @@ def test_norm_and_conv_checks(kda):
         kda.conv_chunk_prefill(xc, torch.zeros(C, W, dtype=BF), torch.zeros(2, W - 2, C, dtype=BF),
                                torch.zeros(T, H, D, dtype=F32), torch.zeros(T, H, dtype=F32), cu,
                                torch.zeros(2, H, D, D, dtype=F32), idx, torch.zeros(T, H, D, dtype=BF))
+
+
+def test_fused_norm_checks(kda):
+    """The norm arguments of chunk_prefill / conv_chunk_prefill: both tensors
+    or neither, [T, H, dv] in q's dtype, a [dv] weight."""
+    a = prefill_args()
+    gate, z = torch.zeros(T, H, D, dtype=BF), torch.zeros(T, H, D, dtype=BF)
+    with pytest.raises(ValueError, match="needs both norm_gate and norm_out"):
+        call_prefill(kda, a, norm_gate=gate)
+    with pytest.raises(ValueError, match="needs both norm_gate and norm_out"):
+        call_prefill(kda, a, norm_out=z)
+    with pytest.raises(ValueError, match="norm_weight needs norm_gate and norm_out"):
+        call_prefill(kda, a, norm_weight=torch.ones(D, dtype=BF))
+    with pytest.raises(ValueError, match="norm_gate has shape"):
+        call_prefill(kda, a, norm_gate=torch.zeros(T, H, D + 8, dtype=BF), norm_out=z)
+    with pytest.raises(ValueError, match="norm_out has shape"):
+        call_prefill(kda, a, norm_gate=gate, norm_out=torch.zeros(T - 1, H, D, dtype=BF))
+    with pytest.raises(ValueError, match="norm_gate is"):
+        call_prefill(kda, a, norm_gate=torch.zeros(T, H, D, dtype=F32), norm_out=z)
+    with pytest.raises(ValueError, match="norm_weight has shape"):
+        call_prefill(kda, a, norm_gate=gate, norm_out=z, norm_weight=torch.ones(D + 1, dtype=BF))
+    # Every shape right, in host memory: refused before the C call.
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        call_prefill(kda, a, norm_gate=gate, norm_out=z, norm_weight=torch.ones(D, dtype=BF))
