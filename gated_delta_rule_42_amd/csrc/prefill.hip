@@ -1126,14 +1126,17 @@ __device__ __forceinline__ void load_vec8(const float* p, Vec8<float>& x)
     x.a = *reinterpret_cast<const f32x4*>(p);
     x.b = *reinterpret_cast<const f32x4*>(p + 4);
 }
+// Stores of the norm's output rows: written once and read by no one in the
+// launch, so nontemporal (faster than write-back stores here, while
+// nontemporal loads of the gate were slower).
 __device__ __forceinline__ void store_vec8(bf16* p, const float (&x)[8])
 {
-    *reinterpret_cast<bf16x8*>(p) = pack_bf16x8(x);
+    __builtin_nontemporal_store(__builtin_bit_cast(f32x4, pack_bf16x8(x)), reinterpret_cast<f32x4*>(p));
 }
 __device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
 {
-    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p + 4));
 }
 
 // ---------------------------------------------------------------------------
