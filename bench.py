@@ -46,10 +46,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "3eb252ad5f1bd5022a7c5d1a226e24d1f6fb9171cac4503b2b4cb2723a277371",
-              86299151, 73925120),
-    "chain": (_PREFILL_SRC, "3eb252ad5f1bd5022a7c5d1a226e24d1f6fb9171cac4503b2b4cb2723a277371",
-              125878007, 68161946),
+    "intra": (_PREFILL_SRC, "07a0cae0347d6e79fa0545303c3c05cd9f1f7f2cabd3914f252f655b26dbfe9a",
+              86299214, 73925152),
+    "chain": (_PREFILL_SRC, "07a0cae0347d6e79fa0545303c3c05cd9f1f7f2cabd3914f252f655b26dbfe9a",
+              125877938, 68160643),
     "decode": (_DECODE_SRC, "d1f466732a16d50daed458ecaa357f76aaf1a7cd8ac0d8c0bdba30a7451656b4",
                547988774, 539453741),
 }
@@ -65,9 +65,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "3eb252ad5f1bd5022a7c5d1a226e24d1f6fb9171cac4503b2b4cb2723a277371",
+PROFILE_SPLIT = (_PREFILL_SRC, "07a0cae0347d6e79fa0545303c3c05cd9f1f7f2cabd3914f252f655b26dbfe9a",
                  "profiles/prefill_T4096_H16_d128_kernel_trace.md",
-                 {"intra_kernel": 39.47, "chain_kernel": 38.52})
+                 {"intra_kernel": 39.32, "chain_kernel": 38.50})
 
 
 def profile_split():
