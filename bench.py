@@ -50,8 +50,8 @@ MEASURED_TRAFFIC = {
               86299214, 73925152),
     "chain": (_PREFILL_SRC, "07a0cae0347d6e79fa0545303c3c05cd9f1f7f2cabd3914f252f655b26dbfe9a",
               125877938, 68160643),
-    "decode": (_DECODE_SRC, "d1f466732a16d50daed458ecaa357f76aaf1a7cd8ac0d8c0bdba30a7451656b4",
-               547988774, 539453741),
+    "decode": (_DECODE_SRC, "2ecf2ccae33635ff8c6b8c871ad1213cab2e3558b1c22d607228cf5a4518bc49",
+               547988801, 539490942),
 }
 
 

@@ -181,9 +181,12 @@ void kda_decode_kernel(const AT* __restrict__ q, const AT* __restrict__ k,
 
 // Commit of a speculative step: pool[slot_b] = token_states[b, n_b - 1] for
 // 0 < n_b <= ntok.  One workgroup per (row, head), a streaming copy.
-// 1024 threads: 512 rows x 16 heads of 128 x 128 fp32 states commit in
-// 154.7 us on MI355X (166 us with 256 threads, 159 with 512).
+// 1024 threads, each with all its vectors' loads in flight before it stores
+// any: 512 rows x 16 heads of 128 x 128 fp32 states commit in 148.8 us on
+// MI355X (155 us with one load in flight per thread; 166 us with 256
+// threads, 159 with 512).
 constexpr int kCommitThreads = 1024;
+constexpr int kCommitUnroll = 4;
 
 template <typename ST>
 __global__ __launch_bounds__(kCommitThreads)
@@ -197,10 +200,16 @@ void kda_spec_commit_kernel(const ST* __restrict__ token_states, int heads, int 
     if (slot < 0 || slot >= num_slots || n <= 0 || n > ntok) return;
     const ST* src = token_states + (((int64_t)b * ntok + n - 1) * heads + h) * elems;
     ST* dstp = pool + ((int64_t)slot * heads + h) * elems;
-    for (int64_t i = 4 * (int64_t)threadIdx.x; i < elems; i += 4 * kCommitThreads) {
-        float x[4];
-        load4_stream(src + i, x);
-        store4_stream(dstp + i, x);
+    // kCommitUnroll vectors per thread in flight before any is stored.
+    constexpr int64_t kStep = 4 * (int64_t)kCommitThreads;
+    for (int64_t i0 = 4 * (int64_t)threadIdx.x; i0 < elems; i0 += kStep * kCommitUnroll) {
+        float x[kCommitUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kCommitUnroll; ++u)
+            if (i0 + u * kStep < elems) load4_stream(src + i0 + u * kStep, x[u]);
+#pragma unroll
+        for (int u = 0; u < kCommitUnroll; ++u)
+            if (i0 + u * kStep < elems) store4_stream(dstp + i0 + u * kStep, x[u]);
     }
 }
 
