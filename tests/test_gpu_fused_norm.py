@@ -94,6 +94,20 @@ def test_fused_norm_equals_prefill_then_norm(label, args, wseed):
     say(f"  {label}: fused norm == prefill then norm, bit for bit")
 
 
+def test_fused_norm_varlen_full_size():
+    """The 8-sequence varlen batch (up to 16384 tokens, 16 heads, d = 128,
+    checkpoints every 1024): 2048 chain workgroups, more than the chip holds
+    at once, so the output workgroups of later pairs start only as earlier
+    ones finish.  Everything bit for bit the plain call + the standalone norm."""
+    case = wl.varlen_prefill()
+    a = _run_plain(case, norm=True, wseed=9)
+    b = _run_plain(case, norm=False, wseed=9)
+    for name, u, v in zip(("out", "pool", "checkpoints", "norm out"), a, b):
+        _same(u, v, name, case.name)
+    assert not torch.isnan(a[3].float()).any()
+    say(f"  {case.name}: fused norm == prefill then norm, bit for bit")
+
+
 # ---------------------------------------------------------------- conv front end
 
 def _run_conv(fc, *, norm: bool, wseed, eps=1e-6):
