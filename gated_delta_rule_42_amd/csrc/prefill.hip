@@ -1152,12 +1152,15 @@ __device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
 //                      Each chunk's S (at its start) and D go, in bf16, to the
 //                      chunk's exchange slot in the workspace; once they have
 //                      landed in L2 the chunk count is published in a flag.
-//   output workgroup   4 output waves and a loader wave (waves 5-7 end at
-//   (blockIdx.z = 1)   once), one barrier per chunk.  The loader waits for the flag and copies the
+//   output workgroup   4 output waves and a loader wave, one barrier per
+//   (blockIdx.z = 1)   chunk.  The loader waits for the flag and copies the
 //                      chunk's S and D from its slot into LDS, two chunks
 //                      ahead; output wave t writes O = scale (Q~ S + Aqk D)
 //                      for token tile t, computed transposed so each lane
-//                      stores 4 consecutive columns.
+//                      stores 4 consecutive columns.  Waves 5-7 end at once,
+//                      or, with the gated norm fused (NORM, a one-dimensional
+//                      grid), waves 5 and 6 normalise this tile's share of
+//                      the rows nine chunks behind (norm_rows).
 // Every byte of a record is an MFMA operand of exactly one wave, so each
 // compute wave loads its own record operands straight into a register ring
 // kChainBufs - 1 chunks ahead.  Splitting the roles halves what one CU pulls
@@ -1167,8 +1170,9 @@ __device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
 // MFMA chain of phase 2: the chain kernel takes 38 us instead of 44 us at
 // T = 4096, H = 16, d = 128.
 //
-// The exchange goes through the XCD's L2: plain stores, and loads that skip
-// the CU's L1.  Workgroups are dealt to the XCDs round-robin by linear id and
+// The exchange goes through the XCD's L2: plain stores, and loads issued only
+// after the flag, at addresses the CU has not read before in the launch.
+// Workgroups are dealt to the XCDs round-robin by linear id and
 // the two roles of a tile are 8 * k ids apart, so they share an XCD.  The
 // flag carries the state workgroup's XCD id and the output workgroup checks
 // it; if the two ever ran on different XCDs the output workgroup would never
@@ -1327,10 +1331,11 @@ struct StoredFlags {
 // it loaded a step before, so it rarely waits), which covers the chunk with a
 // step to spare.  After the loop the waves wait until every tile has stored
 // all its chunks and write the rest.
-// Every step issues the same memory operations (the y store included: a lane
-// without a row of its own stores the value of a row that exists, which
-// another lane stores too), so the compiler's waits for the loads of one
-// step never hold for those of a later one.
+// The steps before the first write and the steps after it run as two loops,
+// and every step of a loop issues the same memory operations (the y store
+// included: a lane without a row of its own stores the value of a row that
+// exists, which another lane stores too), so the compiler's waits for the
+// loads of one step never hold for those of a later one.
 constexpr int kNormLag = 9;   // a multiple of kChainBufs: the write steps start on a ring boundary
 constexpr int kNormCheckLag = 4;   // the loader's check at the end of step c covers c - 4 chunks
 
@@ -1724,7 +1729,7 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     // With the norm fused the pair's output workgroups also publish, per
     // tile, how many chunks of o are stored (in L2, two steps late), and each
     // normalises its share of every chunk's rows once all tiles have stored
-    // them: waves 5 and on (see norm_rows below).  Other waves past the loader
+    // them: waves 5 and on (norm_rows, above).  Other waves past the loader
     // have no work.
     uint32_t* const nflag0 = NORM ? reinterpret_cast<uint32_t*>(ws + nrm.flag_off) + ((int64_t)seq * heads + h) * (D / 16)
                                   : nullptr;
