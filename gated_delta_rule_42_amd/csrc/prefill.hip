@@ -1145,7 +1145,7 @@ __device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
 // Two workgroups per (sequence, head, 16-column d_v tile), on two CUs of one
 // XCD:
 //   state workgroup    8 waves, two barriers per chunk.  Phase 1: wave w <
-//   (blockIdx.z = 0)   BT / 16 computes D = U - W S for token tile w; phase 2:
+//                      BT / 16 computes D = U - W S for token tile w; phase 2:
 //                      every wave w computes S <- e^{G_C} S + Kb^T D for key
 //                      tile w (and w + 8, ... for d_k > 128).  S stays in fp32
 //                      accumulators and is shared as bf16 through LDS.
@@ -1153,14 +1153,14 @@ __device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
 //                      chunk's exchange slot in the workspace; once they have
 //                      landed in L2 the chunk count is published in a flag.
 //   output workgroup   4 output waves and a loader wave, one barrier per
-//   (blockIdx.z = 1)   chunk.  The loader waits for the flag and copies the
+//                      chunk.  The loader waits for the flag and copies the
 //                      chunk's S and D from its slot into LDS, two chunks
 //                      ahead; output wave t writes O = scale (Q~ S + Aqk D)
 //                      for token tile t, computed transposed so each lane
 //                      stores 4 consecutive columns.  Waves 5-7 end at once,
-//                      or, with the gated norm fused (NORM, a one-dimensional
-//                      grid), waves 5 and 6 normalise this tile's share of
-//                      the rows nine chunks behind (norm_rows).
+//                      or, with the gated norm fused (NORM), waves 5 and 6
+//                      normalise this tile's share of the rows nine chunks
+//                      behind (norm_rows).
 // Every byte of a record is an MFMA operand of exactly one wave, so each
 // compute wave loads its own record operands straight into a register ring
 // kChainBufs - 1 chunks ahead.  Splitting the roles halves what one CU pulls
@@ -1177,8 +1177,9 @@ __device__ __forceinline__ void store_vec8(float* p, const float (&x)[8])
 // flag carries the state workgroup's XCD id and the output workgroup checks
 // it; if the two ever ran on different XCDs the output workgroup would never
 // see the flag move and writes NaN after a bounded wait instead of stale
-// results.  State workgroups come first in the grid, so every output
-// workgroup's producer is already running when it starts waiting.
+// results.  A pair's state workgroups come before its output workgroups in
+// the grid, so every output workgroup's producer is already running when it
+// starts waiting.
 constexpr int kChainWaves = 8;
 constexpr int kChainThreads = kChainWaves * kWave;
 constexpr int kChainBufs = 3;                      // register ring depth (chunks)
@@ -1453,28 +1454,25 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     __shared__ __attribute__((aligned(16))) bf16 sD[16][DP];      // state: bf16 D^T
     __shared__ __attribute__((aligned(1024))) uint8_t sX[kXchStages][XSLOT];   // output: S, D
 
-    // Without the norm, blockIdx.x enumerates (sequence, head) pairs, padded
-    // to a multiple of 8, blockIdx.y the column tile and blockIdx.z the role.
-    // With it, the grid is one-dimensional: the state plane, then the output
-    // plane, each in blocks of 8 pairs x D/16 tiles with the pair fastest.
-    // Either way a pair's workgroups are 8 * k ids apart (one XCD), and with
-    // the norm the output workgroups of a pair, which wait for one another,
-    // sit in one block of 8 D/16 consecutive ids: blocks are dispatched in
-    // order, so the earliest unfinished block always gets the next free
-    // slots and its members are resident together.
-    int pair, tile;
-    bool state_role;
-    if constexpr (NORM) {
-        const int plane = (int)(gridDim.x / 2u), id = (int)(blockIdx.x % (unsigned)plane);
-        state_role = blockIdx.x < (unsigned)plane;
-        const int r = id % (8 * (D / 16));
-        pair = id / (8 * (D / 16)) * 8 + r % 8;
-        tile = r / 8;
-    } else {
-        pair = blockIdx.x;
-        tile = blockIdx.y;
-        state_role = blockIdx.z == 0;
-    }
+    // One-dimensional grid in blocks of 8 (sequence, head) pairs (padded to a
+    // multiple of 8): a block holds the state workgroups of its pairs' D/16
+    // tiles, then their output workgroups, pair fastest in both.  So a pair's
+    // workgroups are 8 * k ids apart (one XCD), every output workgroup comes
+    // after its producer, and the chip works through the pairs block by
+    // block: the eight tiles of a pair read its records from L2 at about the
+    // same time and its output workgroups run beside its state workgroups.
+    // (With the state workgroups of all pairs first, a batch larger than the
+    // chip ran its state roles tile by tile in rounds, each round reading the
+    // records again, and the output roles only after them.)  With the norm
+    // the output workgroups of a pair also wait for one another; they sit in
+    // one block, blocks are dispatched in order, and a workgroup waits only
+    // for its own block and earlier ones, so the earliest unfinished block
+    // always gets the next free slots.
+    constexpr int TB = 8 * (D / 16);               // workgroups of one role in a block
+    const int blk = (int)(blockIdx.x / (2u * TB)), rb = (int)(blockIdx.x % (2u * TB));
+    const bool state_role = rb < TB;
+    const int rr = state_role ? rb : rb - TB;
+    const int pair = blk * 8 + rr % 8, tile = rr / 8;
     if (pair >= n_seqs * heads) return;
     const int seq = pair / heads, h = pair % heads, n0 = tile * 16;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -1959,9 +1957,9 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     nrm.eps = a.norm_eps;
     nrm.flag_off = lay.nflag_off;
     const int spin = (a.flags & KDA_FLAG_DIAG_GIVE_UP) ? 0 : kMaxSpin;
+    const int64_t plane = pairs * (D / 16);         // workgroups of one role
+    if (2 * plane > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
     if (norm) {
-        const int64_t plane = pairs * (D / 16);
-        if (2 * plane > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
         hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, true>), dim3((unsigned)(2 * plane)),
                            dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                            static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
@@ -1969,7 +1967,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                            static_cast<AT*>(a.out), a.out_stride, ws,
                            lay.xch_off, lay.chunks, lay.flag_off, status, spin, nrm);
     } else {
-        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, false>), dim3((unsigned)pairs, (unsigned)(D / 16), 2u),
+        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, false>), dim3((unsigned)(2 * plane)),
                            dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                            static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                            static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,

@@ -1,22 +1,23 @@
 """Placement of the chain kernel's workgroups (host logic, no GPU).
 
-The two workgroups of a state tile -- the state role (blockIdx.z = 0), which
-publishes each chunk's S and D, and the output role (z = 1), which waits for
-them -- pass data through the XCD's L2, so they must run on one XCD, and the
-producer must be dispatched before its consumer so that the consumer's
-bounded wait always ends.  The GPU deals the workgroups of a launch to its 8
-XCDs round-robin by linear id x + X (y + Y z) and dispatches them in
-linear-id order.  This test checks that the chain kernel's source launches
-the grid modelled here, then enumerates that grid for every shape the tests
-and the bench launch (and more) and checks both properties.
+The two workgroups of a state tile -- the state role, which publishes each
+chunk's S and D, and the output role, which waits for them -- pass data
+through the XCD's L2, so they must run on one XCD, and the producer must be
+dispatched before its consumer so that the consumer's bounded wait always
+ends.  The GPU deals the workgroups of a launch to its 8 XCDs round-robin by
+linear id and dispatches them in linear-id order.  This test checks that the
+chain kernel's source launches the grid modelled here, then enumerates that
+grid for every shape the tests and the bench launch (and more) and checks
+both properties.
 
-With the gated norm fused, the grid is one-dimensional (the state plane, then
-the output plane, each in blocks of 8 pairs x d/16 tiles, pair fastest) and
-the output workgroups of a pair also wait for one another.  Besides the two
-properties above, a pair's workgroups must then all share one XCD and its
-output workgroups lie in one block of 8 d/16 consecutive ids, so that the
-earliest unfinished block, whose members wait only for each other and for
-earlier workgroups, is always dispatched whole."""
+The grid is one-dimensional, in blocks of 8 (sequence, head) pairs: the
+state workgroups of the block's pairs and d/16 tiles, then their output
+workgroups, pair fastest in both.  With the gated norm fused the output
+workgroups of a pair also wait for one another, so besides the two
+properties above a pair's workgroups must all share one XCD and its output
+workgroups lie in one block, whose members wait only for each other and for
+earlier workgroups: dispatch in id order can then always finish the earliest
+unfinished block."""
 import os
 import re
 
@@ -27,29 +28,34 @@ SRC = os.path.join(ROOT, "gated_delta_rule_42_amd", "csrc", "prefill.hip")
 XCDS = 8
 
 
-def chain_grid(num_seqs: int, heads: int, d: int):
-    """(X, Y, Z) of the chain kernel's launch: (sequence, head) pairs padded to
-    a multiple of 8, the 16-column tiles of d_v, the two roles."""
+def chain_grid(num_seqs: int, heads: int, d: int) -> int:
+    """Workgroups of the chain kernel's launch: (sequence, head) pairs padded
+    to a multiple of 8, times the 16-column tiles of d_v, times the two roles."""
     pairs = (num_seqs * heads + 7) // 8 * 8
-    return pairs, d // 16, 2
+    return 2 * pairs * (d // 16)
+
+
+def grid_decode(L: int, d: int):
+    """(pair, tile, state_role) of linear id L, as the kernel computes it."""
+    tb = 8 * (d // 16)
+    blk, rb = divmod(L, 2 * tb)
+    state = rb < tb
+    rr = rb if state else rb - tb
+    return blk * 8 + rr % 8, rr // 8, state
 
 
 def test_source_launches_the_modelled_grid():
     src = open(SRC).read()
     assert "const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;" in src
-    assert re.search(r"chain_kernel<D, BT, AT, ST, false>\)\s*,\s*dim3\(\(unsigned\)pairs, \(unsigned\)\(D / 16\), 2u\)",
-                     src), "chain_kernel launch geometry changed"
-    assert "pair = blockIdx.x;" in src
-    assert "tile = blockIdx.y;" in src
-    assert "state_role = blockIdx.z == 0;" in src
-    # The fused-norm grid.
     assert "const int64_t plane = pairs * (D / 16);" in src
-    assert re.search(r"chain_kernel<D, BT, AT, ST, true>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)", src)
-    for line in ("const int plane = (int)(gridDim.x / 2u), id = (int)(blockIdx.x % (unsigned)plane);",
-                 "state_role = blockIdx.x < (unsigned)plane;",
-                 "const int r = id % (8 * (D / 16));",
-                 "pair = id / (8 * (D / 16)) * 8 + r % 8;",
-                 "tile = r / 8;"):
+    for norm in ("false", "true"):
+        assert re.search(r"chain_kernel<D, BT, AT, ST, %s>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)" % norm,
+                         src), f"chain_kernel<..., {norm}> launch geometry changed"
+    for line in ("constexpr int TB = 8 * (D / 16);",
+                 "const int blk = (int)(blockIdx.x / (2u * TB)), rb = (int)(blockIdx.x % (2u * TB));",
+                 "const bool state_role = rb < TB;",
+                 "const int rr = state_role ? rb : rb - TB;",
+                 "const int pair = blk * 8 + rr % 8, tile = rr / 8;"):
         assert line in src, line
 
 
@@ -64,50 +70,26 @@ SHAPES = sorted({
 
 
 @pytest.mark.parametrize("n,h,d", SHAPES)
-def test_tile_roles_share_an_xcd_and_the_producer_comes_first(n, h, d):
-    X, Y, Z = chain_grid(n, h, d)
-    assert X % XCDS == 0
-    lin = lambda x, y, z: x + X * (y + Y * z)
-    for x in range(n * h):                     # workgroups past n*h return at once
-        for y in range(Y):
-            producer, consumer = lin(x, y, 0), lin(x, y, 1)
-            assert producer % XCDS == consumer % XCDS
-            assert producer < consumer
-
-
-def test_varlen_batch_grid_size():
-    X, Y, Z = chain_grid(8, 16, 128)
-    assert X * Y * Z == 2048
-
-
-def norm_grid_decode(L: int, plane: int, d: int):
-    """(pair, tile, state_role) of linear id L in the fused-norm grid, as the
-    kernel computes it."""
+def test_grid_placement(n, h, d):
+    total = chain_grid(n, h, d)
     Y = d // 16
-    i = L % plane
-    r = i % (8 * Y)
-    return i // (8 * Y) * 8 + r % 8, r // 8, L < plane
-
-
-@pytest.mark.parametrize("n,h,d", SHAPES)
-def test_norm_grid_placement(n, h, d):
-    X, Y, _ = chain_grid(n, h, d)
-    plane = X * Y
     seen = {}
-    for L in range(2 * plane):
-        pair, tile, state = norm_grid_decode(L, plane, d)
-        assert 0 <= tile < Y and 0 <= pair < X
+    for L in range(total):
+        pair, tile, state = grid_decode(L, d)
+        assert 0 <= tile < Y and 0 <= pair < total // (2 * Y)
         seen[(pair, tile, state)] = L
-    assert len(seen) == 2 * plane                       # every (pair, tile, role) once
-    block = 8 * Y
-    for pair in range(n * h):
+    assert len(seen) == total                             # every (pair, tile, role) once
+    block = 2 * 8 * Y
+    for pair in range(n * h):                             # workgroups past n*h return at once
         ids = [seen[(pair, t, s)] for t in range(Y) for s in (True, False)]
         assert len({L % XCDS for L in ids}) == 1           # one XCD for the whole pair
         for t in range(Y):
             assert seen[(pair, t, True)] < seen[(pair, t, False)]   # producer first
-        outs = [seen[(pair, t, False)] - plane for t in range(Y)]
-        assert len({o // block for o in outs}) == 1        # one block of the output plane
-    # Output workgroups wait only on their own block and on earlier ids (the
-    # state plane), so dispatch in id order can always finish the earliest
-    # unfinished block: it needs 8 d/16 <= 64 slots.
-    assert block <= 64
+        assert len({L // block for L in ids}) == 1          # one block holds the pair
+    # A block is at most 2 x 8 x 8 = 128 workgroups: half of what the
+    # chip holds at one chain workgroup per CU.
+    assert block <= 128
+
+
+def test_varlen_batch_grid_size():
+    assert chain_grid(8, 16, 128) == 2048
