@@ -1463,13 +1463,18 @@ void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ po
     // same time and its output workgroups run beside its state workgroups.
     // (With the state workgroups of all pairs first, a batch larger than the
     // chip ran its state roles tile by tile in rounds, each round reading the
-    // records again, and the output roles only after them.)  With the norm
+    // records again, and the output roles only after them.)  The blocks run
+    // last pair first: the intra kernel writes the records in pair order, so
+    // the last pairs' records are the newest and most likely still in the
+    // memory-side cache when a large batch's records do not all fit there.
+    // With the norm
     // the output workgroups of a pair also wait for one another; they sit in
     // one block, blocks are dispatched in order, and a workgroup waits only
     // for its own block and earlier ones, so the earliest unfinished block
     // always gets the next free slots.
     constexpr int TB = 8 * (D / 16);               // workgroups of one role in a block
-    const int blk = (int)(blockIdx.x / (2u * TB)), rb = (int)(blockIdx.x % (2u * TB));
+    const int blk = (int)(gridDim.x / (2u * TB)) - 1 - (int)(blockIdx.x / (2u * TB));
+    const int rb = (int)(blockIdx.x % (2u * TB));
     const bool state_role = rb < TB;
     const int rr = state_role ? rb : rb - TB;
     const int pair = blk * 8 + rr % 8, tile = rr / 8;

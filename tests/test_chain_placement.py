@@ -10,9 +10,9 @@ chain kernel's source launches the grid modelled here, then enumerates that
 grid for every shape the tests and the bench launch (and more) and checks
 both properties.
 
-The grid is one-dimensional, in blocks of 8 (sequence, head) pairs: the
-state workgroups of the block's pairs and d/16 tiles, then their output
-workgroups, pair fastest in both.  With the gated norm fused the output
+The grid is one-dimensional, in blocks of 8 (sequence, head) pairs, the last
+block first: the state workgroups of the block's pairs and d/16 tiles, then
+their output workgroups, pair fastest in both.  With the gated norm fused the output
 workgroups of a pair also wait for one another, so besides the two
 properties above a pair's workgroups must all share one XCD and its output
 workgroups lie in one block, whose members wait only for each other and for
@@ -35,10 +35,12 @@ def chain_grid(num_seqs: int, heads: int, d: int) -> int:
     return 2 * pairs * (d // 16)
 
 
-def grid_decode(L: int, d: int):
-    """(pair, tile, state_role) of linear id L, as the kernel computes it."""
+def grid_decode(L: int, total: int, d: int):
+    """(pair, tile, state_role) of linear id L in a grid of `total`
+    workgroups, as the kernel computes it (blocks last pair first)."""
     tb = 8 * (d // 16)
-    blk, rb = divmod(L, 2 * tb)
+    blk = total // (2 * tb) - 1 - L // (2 * tb)
+    rb = L % (2 * tb)
     state = rb < tb
     rr = rb if state else rb - tb
     return blk * 8 + rr % 8, rr // 8, state
@@ -52,7 +54,8 @@ def test_source_launches_the_modelled_grid():
         assert re.search(r"chain_kernel<D, BT, AT, ST, %s>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)" % norm,
                          src), f"chain_kernel<..., {norm}> launch geometry changed"
     for line in ("constexpr int TB = 8 * (D / 16);",
-                 "const int blk = (int)(blockIdx.x / (2u * TB)), rb = (int)(blockIdx.x % (2u * TB));",
+                 "const int blk = (int)(gridDim.x / (2u * TB)) - 1 - (int)(blockIdx.x / (2u * TB));",
+                 "const int rb = (int)(blockIdx.x % (2u * TB));",
                  "const bool state_role = rb < TB;",
                  "const int rr = state_role ? rb : rb - TB;",
                  "const int pair = blk * 8 + rr % 8, tile = rr / 8;"):
@@ -75,7 +78,7 @@ def test_grid_placement(n, h, d):
     Y = d // 16
     seen = {}
     for L in range(total):
-        pair, tile, state = grid_decode(L, d)
+        pair, tile, state = grid_decode(L, total, d)
         assert 0 <= tile < Y and 0 <= pair < total // (2 * Y)
         seen[(pair, tile, state)] = L
     assert len(seen) == total                             # every (pair, tile, role) once
