@@ -14,6 +14,8 @@ warm-up calls from idle, ~82 µs after 200), so a short warm-up would time the
 ramp rather than the kernels.  To keep the inputs coming from HBM rather than from the 256 MB
 last-level cache, the calls rotate over four independent copies of the
 activations (each ~80 MB).  The same line carries:
+  * varlen: tokens/s of the varlen batch (8 sequences of 256-4096 tokens,
+    bf16 pool, checkpoints every 1024 tokens), one prefill call per step;
   * decode: seq/s for 512 sequences x 1 token on an fp32 pool of 1024 slots;
   * spec: speculative decode of the same batch with 4 draft tokens per row
     (draft tokens/s; state after every token written), and its commit;
@@ -194,6 +196,37 @@ def bench_prefill(steps: int, warmup: int):
     return case, ms, wall, spread
 
 
+def bench_varlen(steps: int, warmup: int):
+    """The varlen batch: 8 sequences (lengths uniform in [256, 4096]), H=16,
+    d=128, bf16 q/k/v, a 256-slot bf16 pool, checkpoints every 1024 tokens;
+    one prefill call per step."""
+    import torch
+    from gated_delta_rule_42_amd import kda, workloads as wl
+    case = wl.varlen_prefill()
+    dev = "cuda"
+    q, k, v, g, beta = (t.to(dev) for t in (case.q, case.k, case.v, case.g, case.beta))
+    cu, slots = case.cu_seqlens.to(dev), case.slots.to(dev)
+    has_init = None if case.has_init is None else case.has_init.to(dev)
+    pool = case.pool.to(dev)
+    T, H, d = case.total_tokens, case.g.shape[1], case.g.shape[2]
+    out = torch.empty_like(v)
+    ckpt = torch.empty(max(case.ckpt_rows(), 1), H, d, d, dtype=pool.dtype, device=dev)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(case.num_seqs, T, H, d, d, case.chunk_size),
+                     dtype=torch.uint8, device=dev)
+
+    def call(i):
+        kda.chunk_prefill(q, k, v, g, beta, cu, pool, slots, out, workspace=ws,
+                          has_initial_state=has_init, checkpoints=ckpt,
+                          ckpt_interval=case.ckpt_interval, scale=case.scale,
+                          chunk_size=case.chunk_size)
+
+    ms, wall = time_calls(call, steps, warmup)
+    status = kda.chunk_prefill_check(ws)
+    if status != 0:
+        raise RuntimeError(f"varlen prefill reported device status {status:#x}")
+    return case, ms
+
+
 def bench_decode(steps: int, warmup: int):
     import torch
     from gated_delta_rule_42_amd import kda, workloads as wl
@@ -340,7 +373,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "spec", "pipeline", "copy"],
+    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "spec", "pipeline", "copy"],
                     default=None,
                     help="run one leg only (for profiling); prints that leg's numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -398,6 +431,20 @@ def main() -> int:
             "call_us_percentiles": spread,
         })
         progress("prefill")
+    if args.only in (None, "varlen"):
+        vcase, vms = bench_varlen(K, W)
+        T, H, d = vcase.total_tokens, 16, 128
+        n_states = int((vcase.slots >= 0).sum())
+        vbytes = (prefill_alg_bytes(T, H, d, d, 2, 2, n_states)
+                  + vcase.ckpt_rows() * H * d * d * 2)               # the checkpoints written
+        vgbs = vbytes / (vms * 1e-3) / 1e9
+        result["varlen"] = {
+            "value": T / (vms * 1e-3), "unit": "tokens/s", "ms_per_step": vms, "steps": K,
+            "workload": vcase.name + f" ({T} tokens)",
+            "roofline": {"kernel": "whole prefill call (intra_kernel, chain_kernel)", "bound": "hbm",
+                         "achieved": vgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": vgbs / HBM_PEAK_GBS, "alg_bytes": vbytes}}
+        progress("varlen")
     if args.only in (None, "decode"):
         dcase, dms, dwall = bench_decode(K, W)
         B, H, d = 512, 16, 128
