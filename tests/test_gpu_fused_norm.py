@@ -219,3 +219,26 @@ def test_fused_norm_failure_report():
     K.gated_rmsnorm(out2, gate, z3)
     torch.cuda.synchronize()
     assert torch.equal(bits(z2.cpu()), bits(z3.cpu())), "normal call after the give-up differs"
+
+
+def test_many_short_sequences():
+    """64 short sequences (1-300 tokens, two of them padding) x 16 heads, d =
+    128: 1,024 (sequence, head) pairs, 16,384 chain workgroups, many times
+    what the chip holds at once.  The plain prefill against the oracle on
+    every head, and the fused norm bit for bit the plain call + the
+    standalone norm: the grid's dispatch order keeps every wait finite at
+    this scale, the norm waves' waits for their peers included."""
+    from tests.gpu_support import check_prefill, gpu_prefill
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 301, size=64)]
+    slots = rng.choice(96, 64, replace=False).astype(np.int32)
+    slots[[5, 40]] = -1
+    case = wl.random_prefill(31, lengths, 16, 128, 128, n_slots=96, slots=slots,
+                             state_dtype=BF16, ckpt_interval=128, scale=inv_sqrt(128),
+                             state_std=0.3, name="many_short_64seq_H16_d128")
+    check_prefill(case, gpu_prefill(case), label=case.name)
+    a = _run_plain(case, norm=True, wseed=9)
+    b = _run_plain(case, norm=False, wseed=9)
+    for name, u, v in zip(("out", "pool", "checkpoints", "norm out"), a, b):
+        _same(u, v, name, case.name)
+    say(f"  {case.name}: oracle parity, fused norm == prefill then norm, bit for bit")
