@@ -1187,6 +1187,13 @@ constexpr int kXchStages = 3;                      // LDS stages of S and D (out
 // Spin limit of the output workgroup's loader waiting for a chunk; the state
 // workgroup publishes one every microsecond or so, so this is a safety net.
 constexpr int kMaxSpin = 1 << 20;
+// Longest average sequence (in chunks) for which a grid that does not fit on
+// the chip at one workgroup per CU runs two per CU (d = 128).  Packing lets
+// the chains of more sequences run at once, which hides each chain's fixed
+// start and end (a few microseconds), but each CU then serves two
+// workgroups' loads, so every step is slower: on MI355X (H = 16) the packed
+// grid was faster up to ~22 chunks per sequence and slower from 32.
+constexpr int kPackMaxChunks = 24;
 
 // Cache policy sc0 (workgroup scope) of the loader's copies: they read each
 // exchange slot once, after its flag, at an address this CU has not read
@@ -1432,8 +1439,11 @@ __device__ __forceinline__ void norm_rows(int nw, int lane, int tile, int nch, i
         if (j0 + i < nch) write_rows(j0 + i, rest[i]);
 }
 
-template <int D, int BT, typename AT, typename ST, bool NORM>
-__global__ __launch_bounds__(kChainThreads)
+// PACK caps the registers at 128 per lane (four waves per SIMD), so that two
+// workgroups fit on one CU; the host picks it for grids of short sequences
+// that do not fit on the chip at one workgroup per CU (see launch_typed).
+template <int D, int BT, typename AT, typename ST, bool NORM, bool PACK>
+__global__ __launch_bounds__(kChainThreads, PACK ? 4 : 2)
 void chain_kernel(const int32_t* __restrict__ cu, const int64_t* __restrict__ pos, int n_seqs, int heads,
                   ST* __restrict__ pool, int64_t num_slots, const int32_t* __restrict__ slots,
                   const uint8_t* __restrict__ has_init, ST* __restrict__ ckpt, int64_t ckpt_cap,
@@ -1964,15 +1974,36 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     const int spin = (a.flags & KDA_FLAG_DIAG_GIVE_UP) ? 0 : kMaxSpin;
     const int64_t plane = pairs * (D / 16);         // workgroups of one role
     if (2 * plane > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+    bool pack = false;
+    if constexpr (D == 128) {
+        // At d = 128 the chain kernel needs more than 128 registers per lane,
+        // so it runs one workgroup per CU unless compiled with PACK.
+        if (!norm && a.total_tokens <= (int64_t)kPackMaxChunks * BT * a.num_seqs) {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+                pack = 2 * plane > (int64_t)cus;
+            else
+                (void)hipGetLastError();            // fall back to one workgroup per CU
+        }
+    }
     if (norm) {
-        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, true>), dim3((unsigned)(2 * plane)),
+        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, true, false>), dim3((unsigned)(2 * plane)),
                            dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                            static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                            static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
                            static_cast<AT*>(a.out), a.out_stride, ws,
                            lay.xch_off, lay.chunks, lay.flag_off, status, spin, nrm);
+    } else if (pack) {
+        if constexpr (D == 128)
+            hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, false, true>), dim3((unsigned)(2 * plane)),
+                               dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs,
+                               a.heads, static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
+                               static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
+                               static_cast<AT*>(a.out), a.out_stride, ws,
+                               lay.xch_off, lay.chunks, lay.flag_off, status, spin, nrm);
     } else {
-        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, false>), dim3((unsigned)(2 * plane)),
+        hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, false, false>), dim3((unsigned)(2 * plane)),
                            dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                            static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
                            static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,

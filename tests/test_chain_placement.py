@@ -50,9 +50,9 @@ def test_source_launches_the_modelled_grid():
     src = open(SRC).read()
     assert "const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;" in src
     assert "const int64_t plane = pairs * (D / 16);" in src
-    for norm in ("false", "true"):
-        assert re.search(r"chain_kernel<D, BT, AT, ST, %s>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)" % norm,
-                         src), f"chain_kernel<..., {norm}> launch geometry changed"
+    for norm, pack in (("true", "false"), ("false", "true"), ("false", "false")):
+        assert re.search(r"chain_kernel<D, BT, AT, ST, %s, %s>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)"
+                         % (norm, pack), src), f"chain_kernel<..., {norm}, {pack}> launch geometry changed"
     for line in ("constexpr int TB = 8 * (D / 16);",
                  "const int blk = (int)(gridDim.x / (2u * TB)) - 1 - (int)(blockIdx.x / (2u * TB));",
                  "const int rb = (int)(blockIdx.x % (2u * TB));",

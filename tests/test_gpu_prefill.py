@@ -175,6 +175,46 @@ def test_prefill_workspace_reuse():
     check_prefill(small, gpu_prefill(small, workspace=ws), label="workspace reused")
 
 
+def test_packed_chain_equals_per_sequence_calls():
+    """12 sequences of 200-1,500 tokens x 16 heads, d = 128: a chain grid of
+    3,072 workgroups for short sequences, which runs two workgroups per CU.
+    Against the oracle on every head, and bit for bit against 12 calls of one
+    sequence each (256 chain workgroups, one per CU): the packed build
+    computes the same operations."""
+    from gated_delta_rule_42_amd import kda
+    from tests.gpu_support import DEV, assert_device_ok
+    rng = np.random.default_rng(61)
+    lengths = [int(x) for x in rng.integers(200, 1501, size=12)]
+    slots = rng.choice(40, 12, replace=False).astype(np.int32)
+    has_init = [1] * 12
+    has_init[3] = 0
+    case = wl.random_prefill(61, lengths, 16, 128, 128, n_slots=40, slots=slots, has_init=has_init,
+                             state_dtype=F32, scale=inv_sqrt(128), state_std=0.3,
+                             name="packed_12seq_H16_d128")
+    assert case.total_tokens <= 24 * 64 * case.num_seqs      # the packed grid's length bound
+    batch = gpu_prefill(case)
+    check_prefill(case, batch, label=case.name)
+    q, k, v = case.q.to(DEV), case.k.to(DEV), case.v.to(DEV)
+    g, beta = case.g.to(DEV), case.beta.to(DEV)
+    pool = case.pool.to(DEV).clone()
+    out = torch.full(v.shape, float("nan"), dtype=v.dtype, device=DEV)
+    cu = case.cu_seqlens.numpy()
+    for s in range(case.num_seqs):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        one = torch.tensor([0, t1 - t0], dtype=torch.int32, device=DEV)
+        ws = torch.empty(kda.chunk_prefill_workspace_size(1, t1 - t0, 16, 128, 128, 64),
+                         dtype=torch.uint8, device=DEV)
+        kda.chunk_prefill(q[t0:t1], k[t0:t1], v[t0:t1], g[t0:t1], beta[t0:t1], one, pool,
+                          case.slots[s:s + 1].to(DEV), out[t0:t1], workspace=ws,
+                          has_initial_state=case.has_init[s:s + 1].to(DEV), scale=case.scale,
+                          chunk_size=64)
+        torch.cuda.synchronize()
+        assert_device_ok(ws)
+    assert torch.equal(bits(batch[0]), bits(out.cpu())), "packed batch output differs"
+    assert torch.equal(bits(batch[1]), bits(pool.cpu())), "packed batch states differ"
+    say(f"  {case.name}: oracle parity; equal bit for bit to one call per sequence")
+
+
 def test_decode_equals_one_token_prefill():
     case = wl.random_decode(61, 40, 4, 128, 128, n_slots=80)
     o_d, p_d = gpu_decode(case)
