@@ -48,10 +48,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "79ec1c2859c8f6e0380a8f21029476e6f83b8fe90b79a8b727ee97a8880496a9",
-              86325823, 73925152),
-    "chain": (_PREFILL_SRC, "79ec1c2859c8f6e0380a8f21029476e6f83b8fe90b79a8b727ee97a8880496a9",
-              125903213, 68161024),
+    "intra": (_PREFILL_SRC, "ab2bf6e29e6105eec8dbd7702f82e7618928681b5369519ac4938d0b84066608",
+              86309648, 73925152),
+    "chain": (_PREFILL_SRC, "ab2bf6e29e6105eec8dbd7702f82e7618928681b5369519ac4938d0b84066608",
+              125885559, 68160463),
     "decode": (_DECODE_SRC, "2ecf2ccae33635ff8c6b8c871ad1213cab2e3558b1c22d607228cf5a4518bc49",
                547988801, 539490942),
 }
@@ -67,9 +67,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "79ec1c2859c8f6e0380a8f21029476e6f83b8fe90b79a8b727ee97a8880496a9",
+PROFILE_SPLIT = (_PREFILL_SRC, "ab2bf6e29e6105eec8dbd7702f82e7618928681b5369519ac4938d0b84066608",
                  "profiles/prefill_T4096_H16_d128_kernel_trace.md",
-                 {"intra_kernel": 39.57, "chain_kernel": 38.32})
+                 {"intra_kernel": 39.37, "chain_kernel": 38.31})
 
 
 def profile_split():
