@@ -37,6 +37,10 @@
  *   - Results are deterministic: the same call on the same inputs gives
  *     bitwise identical outputs and states (no floating-point atomics), and
  *     which pool slot a sequence uses does not change any value.
+ *   - The prefill entry points read the current device's CU count
+ *     (hipDeviceGetAttribute, no stream work) to choose how densely the
+ *     state-passing kernel is packed on the chip; every choice computes the
+ *     same bits, so a sequence's results do not depend on the batch it is in.
  */
 #ifndef KDA_H_
 #define KDA_H_
