@@ -48,10 +48,10 @@ _PREFILL_SRC = "gated_delta_rule_42_amd/csrc/prefill.hip"
 _DECODE_SRC = "gated_delta_rule_42_amd/csrc/decode.hip"
 MEASURED_TRAFFIC = {
     # kernel: (source, its sha256 when measured, bytes read, bytes written)
-    "intra": (_PREFILL_SRC, "ab2bf6e29e6105eec8dbd7702f82e7618928681b5369519ac4938d0b84066608",
-              86309648, 73925152),
-    "chain": (_PREFILL_SRC, "ab2bf6e29e6105eec8dbd7702f82e7618928681b5369519ac4938d0b84066608",
-              125885559, 68160463),
+    "intra": (_PREFILL_SRC, "1b9d1691c2586b3c687c6317cbf2f38222c0597abe8db49299f37e5fcc140888",
+              86325834, 73925152),
+    "chain": (_PREFILL_SRC, "1b9d1691c2586b3c687c6317cbf2f38222c0597abe8db49299f37e5fcc140888",
+              125879469, 68161377),
     "decode": (_DECODE_SRC, "2ecf2ccae33635ff8c6b8c871ad1213cab2e3558b1c22d607228cf5a4518bc49",
                547988801, 539490942),
 }
@@ -67,9 +67,9 @@ def source_sha256(rel: str) -> str:
 # kernel-trace summary of this bench's prefill leg (source, its sha256 when
 # profiled, {kernel: mean µs}): the split of the call, valid only for the
 # source it was measured on.
-PROFILE_SPLIT = (_PREFILL_SRC, "ab2bf6e29e6105eec8dbd7702f82e7618928681b5369519ac4938d0b84066608",
+PROFILE_SPLIT = (_PREFILL_SRC, "1b9d1691c2586b3c687c6317cbf2f38222c0597abe8db49299f37e5fcc140888",
                  "profiles/prefill_T4096_H16_d128_kernel_trace.md",
-                 {"intra_kernel": 39.37, "chain_kernel": 38.31})
+                 {"intra_kernel": 39.21, "chain_kernel": 38.02})
 
 
 def profile_split():

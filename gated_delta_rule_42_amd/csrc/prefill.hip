@@ -1977,8 +1977,10 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     bool pack = false;
     if constexpr (D == 128) {
         // At d = 128 the chain kernel needs more than 128 registers per lane,
-        // so it runs one workgroup per CU unless compiled with PACK.
-        if (!norm && a.total_tokens <= (int64_t)kPackMaxChunks * BT * a.num_seqs) {
+        // so it runs one workgroup per CU unless compiled with PACK (not for
+        // fp32 activations with the fused norm, whose build needs ~190).
+        const bool packable = !norm || std::is_same<AT, bf16>::value;
+        if (packable && a.total_tokens <= (int64_t)kPackMaxChunks * BT * a.num_seqs) {
             int dev = 0, cus = 0;
             if (hipGetDevice(&dev) == hipSuccess &&
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
@@ -1987,7 +1989,15 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
                 (void)hipGetLastError();            // fall back to one workgroup per CU
         }
     }
-    if (norm) {
+    if (norm && pack) {
+        if constexpr (D == 128 && std::is_same<AT, bf16>::value)
+            hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, true, true>), dim3((unsigned)(2 * plane)),
+                               dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs,
+                               a.heads, static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,
+                               static_cast<ST*>(a.ckpt), a.ckpt_capacity, a.ckpt_interval, a.scale,
+                               static_cast<AT*>(a.out), a.out_stride, ws,
+                               lay.xch_off, lay.chunks, lay.flag_off, status, spin, nrm);
+    } else if (norm) {
         hipLaunchKernelGGL((chain_kernel<D, BT, AT, ST, true, false>), dim3((unsigned)(2 * plane)),
                            dim3(kChainThreads), 0, stream, a.cu_seqlens, a.seq_pos, a.num_seqs, a.heads,
                            static_cast<ST*>(a.pool), a.num_slots, a.slots, a.has_init,

@@ -50,7 +50,7 @@ def test_source_launches_the_modelled_grid():
     src = open(SRC).read()
     assert "const int64_t pairs = ((int64_t)a.num_seqs * a.heads + 7) / 8 * 8;" in src
     assert "const int64_t plane = pairs * (D / 16);" in src
-    for norm, pack in (("true", "false"), ("false", "true"), ("false", "false")):
+    for norm, pack in (("true", "true"), ("true", "false"), ("false", "true"), ("false", "false")):
         assert re.search(r"chain_kernel<D, BT, AT, ST, %s, %s>\)\s*,\s*dim3\(\(unsigned\)\(2 \* plane\)\)"
                          % (norm, pack), src), f"chain_kernel<..., {norm}, {pack}> launch geometry changed"
     for line in ("constexpr int TB = 8 * (D / 16);",

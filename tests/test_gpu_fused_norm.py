@@ -227,9 +227,8 @@ def test_many_short_sequences():
     what the chip holds at once.  The plain prefill against the oracle on
     every head, and the fused norm bit for bit the plain call + the
     standalone norm: the grid's dispatch order keeps every wait finite at
-    this scale, the norm waves' waits for their peers included.  (The plain
-    call's chain runs two workgroups per CU here, the fused one's one per
-    CU, so their o, states and checkpoints also compare the two builds.)"""
+    this scale, the norm waves' waits for their peers included (both calls'
+    chains run two workgroups per CU here)."""
     from tests.gpu_support import check_prefill, gpu_prefill
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.integers(1, 301, size=64)]
